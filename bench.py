@@ -1,0 +1,379 @@
+"""Benchmark of the exact tiled attention kernels on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|ragged|decode16|
+                    decode1|decode4|train|train_w1024] [--no-secondary] [--cpu-seconds S]
+
+Headline (one JSON line on stdout): the dense bf16 causal forward workload (B=4, Hq=Hkv=16,
+N=2048, d=128, causal top-left), reported as causal-adjusted TFLOP/s: 4 * d * (allowed
+query-key pairs over all heads) per forward, with inputs resident in HBM before timing.
+A "step" is one attn_fwd call (the whole forward path: tile scheduling, mask, QK^T, online
+softmax, PV, LSE). Secondary workloads (cached decode GB/s, training fwd+bwd TFLOP/s) are
+measured the same way and reported under "secondary".
+
+Protocol ("Attention Kernel Portability and Benchmarking", fourth and fifth sections):
+outputs are validated against the fp64 oracle on a sample before timing; warm-up calls;
+per-step HIP events on the launch stream give median / p10 / p90 / max; the K timed steps
+are bracketed by device synchronisation. The oracle is timed on the host cores on a bounded
+sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and matrix)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["exact_attention_tiled_amd/csrc/attn_device.hpp",
+                  "exact_attention_tiled_amd/csrc/attn_fwd.hip",
+                  "exact_attention_tiled_amd/csrc/attn_bwd.hip",
+                  "exact_attention_tiled_amd/csrc/attn_internal.h"]
+
+
+# ----------------------------------------------------------------------------------------
+# work accounting
+# ----------------------------------------------------------------------------------------
+
+def row_counts(len_q, len_k, mode, window):
+    """Allowed keys per query position of one sequence (closed form, in-sequence positions)."""
+    i = np.arange(len_q, dtype=np.int64)
+    if mode == wl.MASK_NONE:
+        return np.full(len_q, len_k, dtype=np.int64)
+    end = i if mode == wl.MASK_CAUSAL_TOP_LEFT else i + (len_k - len_q)
+    hi = np.minimum(end, len_k - 1)
+    lo = np.zeros_like(end) if window <= 0 else np.maximum(end - window + 1, 0)
+    return np.maximum(hi - lo + 1, 0)
+
+
+def allowed_pairs(w) -> int:
+    """Allowed (query, key) pairs summed over sequences and query heads."""
+    total = 0
+    for s in range(w.num_seqs):
+        lq = int(w.cu_q[s + 1] - w.cu_q[s])
+        lk = int(w.cu_k[s + 1] - w.cu_k[s])
+        total += int(row_counts(lq, lk, w.mask_mode, w.window).sum())
+    return total * w.hq
+
+
+def fwd_bytes(w) -> int:
+    el = 2 if w.dtype == "bf16" else 4
+    return el * (w.q.size * 2 + w.k.size + w.v.size) + 4 * w.hq * w.total_q
+
+
+def bwd_bytes(w) -> int:
+    el = 2 if w.dtype == "bf16" else 4
+    # reads q, k, v, out, dout, lse; writes dq, dk, dv
+    return el * (w.q.size * 4 + w.k.size * 2 + w.v.size * 2) + 4 * w.hq * w.total_q
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources; None otherwise."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get("entries", {}).get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------------------
+# timing
+# ----------------------------------------------------------------------------------------
+
+def time_steps(fn, steps: int, warmup: int):
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return wall, ms
+
+
+def stats(ms):
+    return {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+            "p90_ms": float(np.percentile(ms, 90)), "max_ms": float(ms.max()),
+            "mean_ms": float(ms.mean())}
+
+
+# ----------------------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------------------
+
+def make_workload(name: str):
+    if name == "dense":
+        return wl.dense_bf16()
+    if name == "ragged":
+        return wl.ragged_gqa()
+    if name.startswith("decode"):
+        return wl.decode(int(name[len("decode"):]))
+    if name == "train":
+        return wl.train_bf16()
+    if name == "train_w1024":
+        return wl.train_bf16(window=1024)
+    raise ValueError(name)
+
+
+def validate_sample(w, out, lse, grads=None):
+    """Outputs checked against the oracle on one (sequence, head group) slice before any
+    timing is interpreted ("Attention Kernel Portability and Benchmarking", fifth section)."""
+    import oracle
+    s = 0
+    grp = w.hq // w.hkv
+    heads = list(range(grp))
+    rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+    ro, rl = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode, w.window,
+                              seqs=[s], heads=heads)
+    o = out.double().cpu().numpy()[rows][:, heads]
+    l = lse.double().cpu().numpy()[heads][:, rows]
+    ok = np.all(np.abs(o - ro[rows][:, heads]) <= 2e-2 + 2e-2 * np.abs(ro[rows][:, heads]))
+    fin = np.isfinite(rl[heads][:, rows])
+    ok &= np.all(np.abs(l[fin] - rl[heads][:, rows][fin]) <= 1e-3)
+    if grads is not None:
+        rq, rk, rv = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale,
+                                          w.mask_mode, w.window, seqs=[s], kv_heads=[0])
+        krows = slice(int(w.cu_k[s]), int(w.cu_k[s + 1]))
+        for g, r, sl, hs in ((grads[0], rq, rows, heads), (grads[1], rk, krows, [0]),
+                             (grads[2], rv, krows, [0])):
+            gg = g.double().cpu().numpy()[sl][:, hs]
+            rr = r[sl][:, hs]
+            ok &= np.all(np.abs(gg - rr) <= 2e-2 + 2e-2 * np.abs(rr))
+    return bool(ok)
+
+
+def bench_forward(w, steps, warmup, validate=True):
+    import torch
+    import exact_attention_tiled_amd as eat
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(w.q).to(dev).to(dt)
+    k = torch.from_numpy(w.k).to(dev).to(dt)
+    v = torch.from_numpy(w.v).to(dev).to(dt)
+    cu_q = torch.from_numpy(w.cu_q).to(dev)
+    cu_k = torch.from_numpy(w.cu_k).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.total_q), dtype=torch.float32, device=dev)
+    wsb = eat.attn_fwd_workspace_size(q, k, cu_q, w.max_seqlen_q, w.max_seqlen_k, w.mask_mode,
+                                      w.window)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    plan = eat.attn_describe_plan(q, k, cu_q, w.max_seqlen_q, w.max_seqlen_k, w.mask_mode, w.window)
+
+    def step():
+        eat.attn_fwd(q, k, v, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
+                     w.window, out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    valid = validate_sample(w, out, lse) if validate else None
+    if validate and not valid:
+        raise SystemExit(f"validation against the oracle failed for {w.name}; not timing it")
+    wall, ms = time_steps(step, steps, warmup)
+    return {"wall_s": wall, "ms": ms, "plan": plan, "validated": valid}
+
+
+def bench_train(w, steps, warmup):
+    import torch
+    import exact_attention_tiled_amd as eat
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (w.q, w.k, w.v, w.dout))
+    cu_q = torch.from_numpy(w.cu_q).to(dev)
+    cu_k = torch.from_numpy(w.cu_k).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.total_q), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsb = eat.attn_bwd_workspace_size(q, k, cu_q, w.max_seqlen_q, w.max_seqlen_k, w.mask_mode,
+                                      w.window)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    fws = torch.empty(1, dtype=torch.uint8, device=dev)
+
+    def fwd():
+        eat.attn_fwd(q, k, v, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
+                     w.window, out=out, lse=lse, workspace=fws)
+
+    def bwd():
+        eat.attn_bwd(q, k, v, out, lse, do, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale,
+                     w.mask_mode, w.window, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    step()
+    torch.cuda.synchronize()
+    if not validate_sample(w, out, lse, grads=(dq, dk, dv)):
+        raise SystemExit(f"validation against the oracle failed for {w.name}; not timing it")
+    wall, ms = time_steps(step, steps, warmup)
+    _, ms_f = time_steps(fwd, steps, 2)
+    _, ms_b = time_steps(bwd, steps, 2)
+    return {"wall_s": wall, "ms": ms, "ms_fwd": ms_f, "ms_bwd": ms_b}
+
+
+# ----------------------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ----------------------------------------------------------------------------------------
+
+def cpu_baseline(w, target_s: float):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity core count
+        threads = len(os.sched_getaffinity(0))
+    grp = w.hq // w.hkv
+    slices = [(s, h) for s in range(w.num_seqs) for h in range(w.hq)]
+    done_pairs = 0
+    t0 = time.perf_counter()
+    n = 0
+    for s, h in slices:
+        oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode, w.window,
+                         seqs=[s], heads=[h])
+        lq = int(w.cu_q[s + 1] - w.cu_q[s])
+        lk = int(w.cu_k[s + 1] - w.cu_k[s])
+        done_pairs += int(row_counts(lq, lk, w.mask_mode, w.window).sum())
+        n += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    flops = 4.0 * w.d * done_pairs
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} of {len(slices)} (sequence, query head) slices of {w.name} "
+                      f"({done_pairs} allowed pairs, {el:.1f} s, float64 numpy, dense-then-mask "
+                      f"per sequence; group size {grp})"}
+
+
+# ----------------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_tiled_amd as eat
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    eat.load()
+
+    w = make_workload(args.workload)
+    pairs = allowed_pairs(w)
+    if args.workload.startswith("decode"):
+        r = bench_forward(w, args.steps, args.warmup)
+        byts = fwd_bytes(w)
+        ms_avg = float(r["ms"].mean())
+        value = byts * args.steps / r["wall_s"] / 1e9
+        metric, unit = "attention decode GB/s (split-K forward)", "GB/s"
+        roof = {"bound": "hbm", "achieved": byts / (ms_avg * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+        kernel = "fwd_splitk_kernel"
+    elif args.workload.startswith("train"):
+        r = bench_train(w, args.steps, args.warmup)
+        flops = 14.0 * w.d * pairs
+        ms_avg = float(r["ms"].mean())
+        value = flops * args.steps / r["wall_s"] / 1e12
+        metric, unit = "attention fwd+bwd TFLOP/s (causal-adjusted)", "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": 10.0 * w.d * pairs / (float(r["ms_bwd"].mean()) * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        kernel = "bwd_main_kernel"
+    else:
+        r = bench_forward(w, args.steps, args.warmup)
+        flops = 4.0 * w.d * pairs
+        ms_avg = float(r["ms"].mean())
+        value = flops * args.steps / r["wall_s"] / 1e12
+        metric, unit = "attention fwd TFLOP/s (causal-adjusted)", "TFLOP/s"
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        roof = {"bound": "mfma", "achieved": flops / (ms_avg * 1e-3) / 1e12, "peak": peak,
+                "unit": "TFLOP/s"}
+        kernel = "fwd_prefill_kernel"
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(kernel, args.workload)
+    roof["kernel"] = kernel
+
+    line = {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["wall_s"] * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded numpy draws, N(0,1), bf16 round-to-nearest-even)",
+        "config": dict(w.describe(), allowed_pairs=pairs, parallelism="single GPU"),
+        "step_stats": stats(r["ms"]), "plan": r.get("plan"), "roofline": roof,
+    }
+    line["config"]["workload"] = w.name
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if not args.no_secondary and args.workload == "dense":
+        sec = []
+        for name in ("decode16", "train"):
+            sw = make_workload(name)
+            sp = allowed_pairs(sw)
+            if name.startswith("decode"):
+                rr = bench_forward(sw, 20, 5)
+                b = fwd_bytes(sw)
+                sec.append({"workload": sw.name, "metric": "decode GB/s", "plan": rr["plan"],
+                            "value": b / (float(np.median(rr["ms"])) * 1e-3) / 1e9,
+                            "frac_of_hbm_peak": b / (float(np.median(rr["ms"])) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            "step_stats": stats(rr["ms"])})
+            else:
+                rr = bench_train(sw, 5, 2)
+                fwd_tf = 4.0 * sw.d * sp / (float(np.median(rr["ms_fwd"])) * 1e-3) / 1e12
+                bwd_tf = 10.0 * sw.d * sp / (float(np.median(rr["ms_bwd"])) * 1e-3) / 1e12
+                tot = 14.0 * sw.d * sp / (float(np.median(rr["ms"])) * 1e-3) / 1e12
+                sec.append({"workload": sw.name, "metric": "fwd+bwd TFLOP/s", "value": tot,
+                            "fwd_tflops": fwd_tf, "bwd_tflops": bwd_tf,
+                            "frac_of_bf16_peak": tot / PEAK_BF16_TFLOPS,
+                            "step_stats": stats(rr["ms"])})
+            del sw
+        line["secondary"] = sec
+    line["env"] = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
+                   "hip": getattr(torch.version, "hip", None), "host": platform.node(),
+                   "library_version": eat.attn_version(), "kernel_source_hash": kernel_source_hash()}
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

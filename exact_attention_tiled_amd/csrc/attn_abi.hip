@@ -1,0 +1,292 @@
+// attn_abi.hip - the C ABI declared in include/attn.h: argument validation, path planning,
+// workspace sizing, device check and kernel launches. No allocation, no global mutable
+// state beyond a once-per-device architecture check.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+using attn::FwdArgs;
+
+struct Plan {
+  int path;        // ATTN_PATH_PREFILL or ATTN_PATH_SPLITK
+  int nsb;         // split-K: key-range blocks per (sequence, K/V head)
+  int chunk;       // split-K: keys per block (multiple of the stage size)
+  size_t workspace;
+};
+
+int validate_common(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
+                    int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
+                    int32_t mode, int32_t window) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_BAD_SHAPE;
+  if (max_q > total_q || max_k > total_k) return ATTN_ERR_BAD_SHAPE;
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return ATTN_ERR_BAD_HEADS;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_BAD_DTYPE;
+  if (mode != ATTN_MASK_NONE && mode != ATTN_MASK_CAUSAL_TOP_LEFT &&
+      mode != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_BAD_MASK;
+  if (window > 0 && mode == ATTN_MASK_NONE) return ATTN_ERR_BAD_MASK;
+  // Element offsets must fit the kernels' 32-bit token indices.
+  if ((long long)total_q * hq * d >= (1LL << 40) || (long long)total_k * hkv * d >= (1LL << 40))
+    return ATTN_ERR_BAD_SHAPE;
+  return ATTN_OK;
+}
+
+// Path choice. Split-K when the query rows of one K/V head fit one wave's two 32-row
+// blocks and the key range is long enough to be worth splitting; prefill otherwise.
+int make_plan(int32_t num_seqs, int32_t total_q, int32_t max_q, int32_t max_k, int32_t hq,
+              int32_t hkv, int32_t d, int32_t path, int32_t num_splits, Plan* plan) {
+  const int group = hq / hkv;
+  const long rows = (long)group * max_q;
+  const bool splitk_ok = rows <= attn::SPLITK_MAX_ROWS;
+  if (path == ATTN_PATH_AUTO) path = (splitk_ok && max_k >= 1024) ? ATTN_PATH_SPLITK : ATTN_PATH_PREFILL;
+  if (path != ATTN_PATH_PREFILL && path != ATTN_PATH_SPLITK) return ATTN_ERR_BAD_PLAN;
+  if (num_splits < 0) return ATTN_ERR_BAD_PLAN;
+  plan->path = path;
+  plan->nsb = 0;
+  plan->chunk = 0;
+  plan->workspace = 0;
+  if (path == ATTN_PATH_PREFILL) return ATTN_OK;
+  if (!splitk_ok) return ATTN_ERR_BAD_PLAN;
+  const int stage = attn::SPLITK_STAGE;
+  const long max_blocks = std::max<long>(1, (max_k + stage - 1) / stage);
+  long nsb = num_splits;
+  if (nsb == 0) {
+    // Aim for about two workgroups per CU over the whole grid, at least 4 stages each.
+    const long units = std::max<long>(1, (long)num_seqs * hkv);
+    nsb = (512 + units - 1) / units;
+    nsb = std::min<long>(nsb, std::max<long>(1, (max_k + 4 * stage - 1) / (4 * stage)));
+  }
+  nsb = std::max<long>(1, std::min<long>(nsb, max_blocks));
+  long chunk = (max_k + nsb - 1) / nsb;
+  chunk = ((chunk + stage - 1) / stage) * stage;
+  if (chunk == 0) chunk = stage;
+  nsb = std::max<long>(1, (max_k + chunk - 1) / chunk);
+  plan->nsb = (int)nsb;
+  plan->chunk = (int)chunk;
+  plan->workspace = attn::splitk_workspace_bytes((int)nsb * 4, total_q, hq, d);
+  return ATTN_OK;
+}
+
+std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_UNSUPPORTED_DEVICE;
+  if (dev < 0 || dev >= 64) return ATTN_ERR_UNSUPPORTED_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_UNSUPPORTED_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? ATTN_OK : ATTN_ERR_UNSUPPORTED_DEVICE;
+}
+
+FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                  const int32_t* cu_k, int32_t num_seqs, int32_t total_q, int32_t total_k,
+                  int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d,
+                  int32_t dtype, float scale, int32_t mode, int32_t window, void* out,
+                  float* lse) {
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.max_q = max_q;
+  a.max_k = max_k;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.dtype = dtype;
+  a.scale = scale;
+  a.mode = mode;
+  a.window = window > 0 ? window : 0;
+  a.out = out;
+  a.lse = lse;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return ATTN_VERSION; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
+    case ATTN_ERR_BAD_SHAPE: return "bad shape (negative size, max_seqlen above total, or head_dim not 64/128)";
+    case ATTN_ERR_BAD_HEADS: return "bad head counts (need Hq >= 1, Hkv >= 1, Hq % Hkv == 0)";
+    case ATTN_ERR_BAD_DTYPE: return "unsupported dtype (ATTN_BF16 or ATTN_F32)";
+    case ATTN_ERR_BAD_MASK: return "bad mask (unknown mode, or window without a causal alignment)";
+    case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query's answer";
+    case ATTN_ERR_UNSUPPORTED_DEVICE: return "current device is not a gfx950 GPU";
+    case ATTN_ERR_LAUNCH_FAILED: return "kernel launch failed";
+    case ATTN_ERR_BAD_SCALE: return "scale is not finite";
+    case ATTN_ERR_BAD_PLAN: return "forced path or split count not usable for this shape";
+    case ATTN_ERR_BAD_RANGE: return "probe window outside the token ranges";
+    default: return "unknown status";
+  }
+}
+
+size_t attn_fwd_ex_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                  int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv,
+                                  int32_t d, int32_t dtype, int32_t mode, int32_t window,
+                                  int32_t path, int32_t num_splits) {
+  if (validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                      window) != ATTN_OK)
+    return 0;
+  Plan plan;
+  if (make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, path, num_splits, &plan) != ATTN_OK)
+    return 0;
+  return plan.workspace;
+}
+
+size_t attn_fwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
+                               int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
+                               int32_t mode, int32_t window) {
+  return attn_fwd_ex_workspace_size(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype,
+                                    mode, window, ATTN_PATH_AUTO, 0);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                const int32_t* cu_k, int32_t num_seqs, int32_t total_q, int32_t total_k,
+                int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
+                float scale, int32_t mode, int32_t window, int32_t path, int32_t num_splits,
+                void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                           window);
+  if (rc != ATTN_OK) return rc;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  Plan plan;
+  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, path, num_splits, &plan);
+  if (rc != ATTN_OK) return rc;
+  if (num_seqs == 0 || total_q == 0) return ATTN_OK;
+  if (!cu_q || !cu_k || !out || !lse || !q) return ATTN_ERR_NULL_PTR;
+  if (total_k > 0 && (!k || !v)) return ATTN_ERR_NULL_PTR;
+  if (plan.workspace > 0 && (!workspace)) return ATTN_ERR_NULL_PTR;
+  if (workspace_bytes < plan.workspace) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  rc = check_device();
+  if (rc != ATTN_OK) return rc;
+  const FwdArgs a = make_args(q, k, v, cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k, hq,
+                              hkv, d, dtype, scale, mode, window, out, lse);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = plan.path == ATTN_PATH_PREFILL
+                     ? attn::launch_fwd_prefill(a, st)
+                     : attn::launch_fwd_splitk(a, plan.nsb, plan.chunk, workspace, st);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+             int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q, int32_t max_k,
+             int32_t hq, int32_t hkv, int32_t d, int32_t dtype, float scale, int32_t mode,
+             int32_t window, void* out, float* lse, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  return attn_fwd_ex(q, k, v, cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d,
+                     dtype, scale, mode, window, ATTN_PATH_AUTO, 0, out, lse, workspace,
+                     workspace_bytes, stream);
+}
+
+size_t attn_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
+                               int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
+                               int32_t mode, int32_t window) {
+  if (validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                      window) != ATTN_OK)
+    return 0;
+  return attn::bwd_workspace_bytes(total_q, hq, d);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs,
+             int32_t total_q, int32_t total_k, int32_t max_q, int32_t max_k, int32_t hq,
+             int32_t hkv, int32_t d, int32_t dtype, float scale, int32_t mode, int32_t window,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                           window);
+  if (rc != ATTN_OK) return rc;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  const size_t need = attn::bwd_workspace_bytes(total_q, hq, d);
+  if (num_seqs == 0 || (total_q == 0 && total_k == 0)) return ATTN_OK;
+  if (!cu_q || !cu_k) return ATTN_ERR_NULL_PTR;
+  if (total_q > 0 && (!q || !out || !lse || !dout || !dq)) return ATTN_ERR_NULL_PTR;
+  if (total_k > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL_PTR;
+  if (need > 0 && !workspace) return ATTN_ERR_NULL_PTR;
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  rc = check_device();
+  if (rc != ATTN_OK) return rc;
+  attn::BwdArgs a;
+  a.f = make_args(q, k, v, cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d,
+                  dtype, scale, mode, window, nullptr, nullptr);
+  a.out = out;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  hipError_t e = attn::launch_bwd(a, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
+}
+
+int attn_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs, int32_t total_q,
+                    int32_t total_k, int32_t mode, int32_t window, int32_t q0, int32_t nq,
+                    int32_t k0, int32_t nk, uint8_t* bits, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0) return ATTN_ERR_BAD_SHAPE;
+  if (mode != ATTN_MASK_NONE && mode != ATTN_MASK_CAUSAL_TOP_LEFT &&
+      mode != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_BAD_MASK;
+  if (window > 0 && mode == ATTN_MASK_NONE) return ATTN_ERR_BAD_MASK;
+  if (q0 < 0 || nq < 0 || k0 < 0 || nk < 0 || (long)q0 + nq > total_q || (long)k0 + nk > total_k)
+    return ATTN_ERR_BAD_RANGE;
+  if (nq == 0 || nk == 0 || num_seqs == 0) return ATTN_OK;
+  if (!cu_q || !cu_k || !bits) return ATTN_ERR_NULL_PTR;
+  int rc = check_device();
+  if (rc != ATTN_OK) return rc;
+  hipError_t e = attn::launch_mask_probe(cu_q, cu_k, num_seqs, mode, window > 0 ? window : 0, q0,
+                                         nq, k0, nk, bits, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
+}
+
+int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
+                       int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
+                       int32_t mode, int32_t window, int32_t path, int32_t num_splits, char* buf,
+                       size_t len) {
+  int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                           window);
+  if (rc != ATTN_OK) return rc;
+  Plan plan;
+  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, path, num_splits, &plan);
+  if (rc != ATTN_OK) return rc;
+  if (!buf || len == 0) return ATTN_ERR_NULL_PTR;
+  const char* dt = dtype == ATTN_BF16 ? "bf16" : "f32";
+  if (plan.path == ATTN_PATH_PREFILL) {
+    FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, num_seqs, total_q, total_k,
+                          max_q, max_k, hq, hkv, d, dtype, 1.0f, mode, window, nullptr, nullptr);
+    std::snprintf(buf, len,
+                  "path=prefill dtype=%s d=%d tile=%dx%d waves=4 grid=%d workspace=0 version=%d",
+                  dt, d, attn::FWD_BM, attn::FWD_BN, attn::fwd_prefill_grid(a), ATTN_VERSION);
+  } else {
+    std::snprintf(buf, len,
+                  "path=splitk dtype=%s d=%d stage=%d rows_per_kvhead<=%d blocks_per_kvhead=%d "
+                  "chunk=%d partials=%d grid=%ld workspace=%zu version=%d",
+                  dt, d, attn::SPLITK_STAGE, (hq / hkv) * max_q, plan.nsb, plan.chunk,
+                  plan.nsb * 4, (long)num_seqs * hkv * plan.nsb, plan.workspace, ATTN_VERSION);
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// attn_internal.h - launch interface between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int num_seqs, total_q, total_k, max_q, max_k;
+  int hq, hkv, d, dtype;
+  float scale;
+  int mode, window;
+  void* out;
+  float* lse;
+};
+
+struct BwdArgs {
+  FwdArgs f;          // q, k, v, cu, sizes, scale, mask (out/lse: forward outputs)
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+};
+
+// Forward prefill tile shape (query rows per workgroup, keys per LDS stage).
+constexpr int FWD_BM = 128;
+constexpr int FWD_BN = 64;
+// Split-K decode: keys per LDS stage (32 per wave) and the largest query-row count per
+// K/V head it supports (two 32-row blocks per wave).
+constexpr int SPLITK_STAGE = 128;
+constexpr int SPLITK_MAX_ROWS = 64;
+
+int fwd_prefill_grid(const FwdArgs& a);
+hipError_t launch_fwd_prefill(const FwdArgs& a, hipStream_t stream);
+
+size_t splitk_workspace_bytes(int nsplit_eff, int total_q, int hq, int d);
+hipError_t launch_fwd_splitk(const FwdArgs& a, int blocks_per_kvh, int chunk, void* workspace,
+                             hipStream_t stream);
+
+hipError_t launch_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int mode,
+                             int window, int q0, int nq, int k0, int nk, uint8_t* bits,
+                             hipStream_t stream);
+
+// Backward tile shape and workspace.
+size_t bwd_workspace_bytes(int total_q, int hq, int d);
+hipError_t launch_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
+
+}  // namespace attn

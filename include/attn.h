@@ -1,0 +1,189 @@
+/*
+ * attn.h - C ABI of the exact tiled attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention over packed ragged sequences
+ * as an I/O-aware tiled HIP kernel: logits Q K^T, exclusion of disallowed pairs, an
+ * online-softmax rescale, P V, and a saved log-sum-exp; the backward pass recomputes P
+ * from that log-sum-exp and produces dQ, dK, dV.
+ *
+ * Operator (per query token t of sequence s, query head h, K/V head g = h / (Hq / Hkv)):
+ *     O[t,h,:]  = sum_u p(t,u) V[u,g,:],   p(t,u) = exp(scale q.k_u - LSE[h,t]) if allowed
+ *     LSE[h,t]  = log sum_{allowed u} exp(scale q_t.k_u)       (natural log)
+ * A row with no allowed key gives O = +0.0 and LSE = -inf.
+ *   - Efficient Attention: Formal Correctness, "The FlashAttention Proof": the tiled kernel
+ *     computes exactly the naive specification; the online recurrence keeps a running max,
+ *     rescales the denominator and accumulator when it moves, and divides at the end.
+ *   - Causal Mask and Ragged Sequence Layouts, sections 1-4: a pair is allowed only inside
+ *     one sequence, compared on in-sequence positions (never on packed offsets); out-of-
+ *     range tile lanes never enter the max, denominator or gradient reductions; causal
+ *     alignment is an explicit choice (top-left: j <= i; bottom-right: j <= i + Nk - Nq);
+ *     all-masked rows output zero.
+ *   - Attention Algorithm Error and Complexity Tests, section 3: GQA query heads share K/V
+ *     heads by consecutive grouping and their K/V gradients are summed.
+ *   - Window (a bounded window is named in the same page's fifth section without a
+ *     formula): width W > 0 keeps keys with position in (end - W, end], where end is the
+ *     aligned diagonal (pos_q for top-left, pos_q + Nk - Nq for bottom-right).
+ *
+ * Layout (all row-major, contiguous, head_dim fastest):
+ *   q, out, dout, dq : [total_q, Hq, head_dim]     element type `dtype`
+ *   k, v, dk, dv     : [total_k, Hkv, head_dim]    element type `dtype`
+ *   lse              : [Hq, total_q]               float32, natural-log units
+ *   cu_seqlens_q/k   : [num_seqs + 1] int32, cu[0] = 0, nondecreasing, cu[num_seqs] =
+ *                      total_q / total_k. Sequence s owns tokens [cu[s], cu[s+1]); zero-
+ *                      length sequences are allowed.
+ *
+ * Ownership: every pointer is caller-owned DEVICE memory (cu_seqlens included). The
+ * library never allocates or frees memory and keeps no pointer after a call returns. Calls
+ * are asynchronous on `stream` (a hipStream_t; NULL = the default stream): results are
+ * valid once that stream has been synchronised. Outputs must not alias inputs. Calls on
+ * different streams are independent when their workspaces and outputs differ.
+ *
+ * Errors: every entry point validates its arguments on the host before launching anything
+ * and returns ATTN_OK (0) or a negative attn_status; on error no output is written. There
+ * is no fallback path: an unsupported combination is an error. Malformed cu_seqlens
+ * contents (device memory, not read by the host) are undefined behaviour.
+ */
+#ifndef EXACT_ATTENTION_TILED_ATTN_H
+#define EXACT_ATTENTION_TILED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_VERSION 100   /* 1.0.0 */
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_PTR = -1,             /* a required pointer is NULL */
+  ATTN_ERR_BAD_SHAPE = -2,            /* negative size, head_dim not 64/128, max_seqlen < 0 */
+  ATTN_ERR_BAD_HEADS = -3,            /* Hq or Hkv < 1, or Hq % Hkv != 0 */
+  ATTN_ERR_BAD_DTYPE = -4,            /* dtype not ATTN_BF16 / ATTN_F32 */
+  ATTN_ERR_BAD_MASK = -5,             /* unknown mask_mode, or window > 0 without causal */
+  ATTN_ERR_WORKSPACE_TOO_SMALL = -6,  /* workspace_bytes below the size query's answer */
+  ATTN_ERR_UNSUPPORTED_DEVICE = -7,   /* current device is not gfx950 */
+  ATTN_ERR_LAUNCH_FAILED = -8,        /* the HIP runtime rejected a kernel launch */
+  ATTN_ERR_BAD_SCALE = -9,            /* scale is not finite */
+  ATTN_ERR_BAD_PLAN = -10,            /* forced path / split count not usable for the shape */
+  ATTN_ERR_BAD_RANGE = -11            /* mask probe window outside the token ranges */
+} attn_status;
+
+enum attn_dtype { ATTN_BF16 = 0, ATTN_F32 = 1 };
+
+enum attn_mask_mode {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL_TOP_LEFT = 1,      /* key j allowed iff j <= i */
+  ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 2   /* key j allowed iff j <= i + Nk - Nq */
+};
+
+/* Forward paths. AUTO picks PREFILL or SPLITK from the shape; the choice is reported by
+ * attn_describe_plan. */
+enum attn_path { ATTN_PATH_AUTO = 0, ATTN_PATH_PREFILL = 1, ATTN_PATH_SPLITK = 2 };
+
+/*
+ * attn_fwd - forward pass: writes out [total_q, Hq, d] and lse [Hq, total_q].
+ *   q, k, v          inputs (layout above), element type `dtype`
+ *   num_seqs         number of packed sequences (0 = nothing to do, returns ATTN_OK)
+ *   total_q/total_k  token counts (= cu[num_seqs])
+ *   max_seqlen_q/k   host-side upper bounds of the per-sequence lengths (used for grid
+ *                    sizing; a bound below the true maximum is undefined behaviour)
+ *   num_heads_q/kv   Hq, Hkv with Hq % Hkv == 0
+ *   head_dim         64 or 128
+ *   scale            finite multiplier of q.k (usually 1/sqrt(head_dim))
+ *   mask_mode        attn_mask_mode; window > 0 needs a causal mode, window <= 0 = none
+ *   workspace        device scratch of at least attn_fwd_workspace_size(...) bytes (may be
+ *                    NULL when that size is 0); its contents need no initialisation
+ */
+int attn_fwd(const void* q, const void* k, const void* v,
+             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+             int32_t num_seqs, int32_t total_q, int32_t total_k,
+             int32_t max_seqlen_q, int32_t max_seqlen_k,
+             int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t dtype,
+             float scale, int32_t mask_mode, int32_t window,
+             void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t attn_fwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                               int32_t dtype, int32_t mask_mode, int32_t window);
+
+/*
+ * attn_fwd_ex / attn_fwd_ex_workspace_size - the forward pass with the path chosen by the
+ * caller (ATTN_PATH_*) and, for SPLITK, the number of key-range blocks per (sequence,
+ * K/V head) (0 = choose). Exists so tests and experiments can run both paths on the same
+ * inputs; results of every path satisfy the same contract.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v,
+                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                int32_t num_seqs, int32_t total_q, int32_t total_k,
+                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t dtype,
+                float scale, int32_t mask_mode, int32_t window,
+                int32_t path, int32_t num_splits,
+                void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t attn_fwd_ex_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                  int32_t num_heads_q, int32_t num_heads_kv,
+                                  int32_t head_dim, int32_t dtype, int32_t mask_mode,
+                                  int32_t window, int32_t path, int32_t num_splits);
+
+/*
+ * attn_bwd - backward pass of attn_fwd for loss gradient dout: writes dq (like q) and
+ * dk, dv (like k; summed over each GQA group). `out` and `lse` must be the forward's
+ * outputs for the same inputs and the SAME mask arguments (the backward rebuilds the same
+ * logical mask: Causal Mask and Ragged Sequence Layouts, section 6). Keys no query may
+ * attend get dk = dv = 0; empty query rows get dq = 0.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+             int32_t num_seqs, int32_t total_q, int32_t total_k,
+             int32_t max_seqlen_q, int32_t max_seqlen_k,
+             int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t dtype,
+             float scale, int32_t mask_mode, int32_t window,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+size_t attn_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                               int32_t dtype, int32_t mask_mode, int32_t window);
+
+/*
+ * attn_mask_probe - runs the forward kernels' mask unit (tile range selection plus the
+ * per-lane test, with the prefill tile shape) for query tokens [q0, q0 + nq) against key
+ * tokens [k0, k0 + nk) and writes bits[i * nk + j] = 1 if the pair (q0 + i, k0 + j) enters
+ * the softmax, else 0 (uint8, device memory, nq * nk bytes). Exists so the mask can be
+ * compared bit for bit with an explicit mask built from sequence ids and positions.
+ * Returns ATTN_ERR_BAD_RANGE if the window leaves [0, total_q) x [0, total_k).
+ */
+int attn_mask_probe(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int32_t num_seqs, int32_t total_q, int32_t total_k,
+                    int32_t mask_mode, int32_t window,
+                    int32_t q0, int32_t nq, int32_t k0, int32_t nk,
+                    uint8_t* bits, void* stream);
+
+/*
+ * attn_describe_plan - writes a one-line description of what attn_fwd_ex would launch for
+ * these arguments (path, tile shape, split count, grid, workspace, library version) into
+ * buf (NUL-terminated, truncated to len). Returns ATTN_OK or a validation error.
+ */
+int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k,
+                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                       int32_t dtype, int32_t mask_mode, int32_t window,
+                       int32_t path, int32_t num_splits, char* buf, size_t len);
+
+/* Static description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* ATTN_VERSION of the built library. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_TILED_ATTN_H */

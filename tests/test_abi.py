@@ -1,0 +1,119 @@
+"""The C ABI library loads, exports every symbol include/attn.h declares, and rejects invalid
+arguments on the host before any launch (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_tiled_amd as eat
+from exact_attention_tiled_amd import build as eat_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL_PTR, BAD_SHAPE, BAD_HEADS, BAD_DTYPE, BAD_MASK, WS_SMALL = 0, -1, -2, -3, -4, -5, -6
+BAD_SCALE, BAD_PLAN, BAD_RANGE = -9, -10, -11
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(eat_build.LIB_PATH):
+        eat_build.build()
+    return eat.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libattn.so"
+    assert sorted(names) == sorted(eat.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert eat.attn_version() == 100
+    for code in (OK, NULL_PTR, BAD_SHAPE, BAD_HEADS, BAD_DTYPE, BAD_MASK, WS_SMALL, -7, -8,
+                 BAD_SCALE, BAD_PLAN, BAD_RANGE):
+        s = eat.attn_status_string(code)
+        assert s and s != "unknown status"
+    assert eat.attn_status_string(12345) == "unknown status"
+
+
+def _fwd(lib, **kw):
+    a = dict(q=1, k=1, v=1, cu_q=1, cu_k=1, num_seqs=1, total_q=4, total_k=4, max_q=4, max_k=4,
+             hq=2, hkv=1, d=64, dtype=0, scale=0.125, mode=1, window=0, path=0, splits=0,
+             out=1, lse=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_ex(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["num_seqs"],
+                           a["total_q"], a["total_k"], a["max_q"], a["max_k"], a["hq"], a["hkv"],
+                           a["d"], a["dtype"], a["scale"], a["mode"], a["window"], a["path"],
+                           a["splits"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), BAD_SHAPE), (dict(total_q=-1), BAD_SHAPE), (dict(max_q=5), BAD_SHAPE),
+    (dict(hq=3, hkv=2), BAD_HEADS), (dict(hkv=0), BAD_HEADS), (dict(dtype=7), BAD_DTYPE),
+    (dict(mode=3), BAD_MASK), (dict(mode=0, window=4), BAD_MASK),
+    (dict(scale=float("inf")), BAD_SCALE), (dict(scale=float("nan")), BAD_SCALE),
+    (dict(path=9), BAD_PLAN), (dict(path=2, max_q=4, hq=32, hkv=1), BAD_PLAN),
+    (dict(q=None), NULL_PTR), (dict(lse=None), NULL_PTR), (dict(cu_k=None), NULL_PTR),
+])
+def test_fwd_validation(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+
+
+def test_fwd_empty_batch_is_noop(lib):
+    assert _fwd(lib, num_seqs=0, total_q=0, total_k=0, max_q=0, max_k=0, q=None, k=None,
+                v=None, out=None, lse=None, cu_q=None, cu_k=None) == OK
+
+
+def test_fwd_workspace_checks(lib):
+    # split-K needs workspace: too small -> error before any launch
+    need = lib.attn_fwd_ex_workspace_size(2, 2, 4096, 1, 2048, 8, 2, 128, 0, 2, 0, 2, 0)
+    assert need > 0
+    assert _fwd(lib, num_seqs=2, total_q=2, total_k=4096, max_q=1, max_k=2048, hq=8, hkv=2,
+                d=128, mode=2, path=2, ws=1, wsb=need - 1) == WS_SMALL
+    assert lib.attn_fwd_ex_workspace_size(2, 256, 256, 128, 128, 2, 2, 64, 1, 2, 0, 1, 0) == 0
+
+
+def test_bwd_validation(lib):
+    args = [1] * 8 + [1, 4, 4, 4, 4, 2, 1, 64, 0, ctypes.c_float(0.1), 1, 0, 1, 1, 1, None, 0, None]
+    a = list(args)
+    a[15] = 100   # head_dim
+    assert lib.attn_bwd(*a) == BAD_SHAPE
+    a = list(args)
+    a[22] = None  # dk
+    assert lib.attn_bwd(*a) == NULL_PTR
+    a = list(args)
+    assert lib.attn_bwd(*a) in (NULL_PTR, WS_SMALL)  # workspace missing
+    need = lib.attn_bwd_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 0, 1, 0)
+    assert need >= 4 * 2 * 64 * 4
+
+
+def test_mask_probe_validation(lib):
+    assert lib.attn_mask_probe(1, 1, 1, 4, 4, 1, 0, 0, 5, 0, 4, 1, None) == BAD_RANGE
+    assert lib.attn_mask_probe(1, 1, 1, 4, 4, 0, 3, 0, 4, 0, 4, 1, None) == BAD_MASK
+    assert lib.attn_mask_probe(1, 1, 1, 4, 4, 1, 0, 0, 0, 0, 4, 1, None) == OK
+    assert lib.attn_mask_probe(1, 1, 1, 4, 4, 1, 0, 0, 4, 0, 4, None, None) == NULL_PTR
+
+
+def test_describe_plan(lib):
+    buf = ctypes.create_string_buffer(256)
+    assert lib.attn_describe_plan(4, 8192, 8192, 2048, 2048, 16, 16, 128, 0, 1, 0, 0, 0, buf, 256) == OK
+    assert buf.value.startswith(b"path=prefill")
+    assert lib.attn_describe_plan(16, 256, 524288, 16, 32768, 32, 8, 128, 0, 2, 0, 0, 0, buf, 256) == OK
+    assert buf.value.startswith(b"path=splitk")
+    assert lib.attn_describe_plan(16, 1024, 512, 64, 32, 32, 8, 128, 0, 2, 0, 0, 0, buf, 256) == OK
+    assert buf.value.startswith(b"path=prefill")
+
+
+def test_build_command_targets_gfx950():
+    cmd = eat_build.compile_command("/tmp/x.so")
+    assert "--offload-arch=gfx950" in cmd
+    assert "-packed-fp32-ops" in cmd

@@ -1,0 +1,126 @@
+"""GPU backward parity against the fp64 oracle, GQA group sums, canaries (bf16)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import BF16_TOL, assert_close, run_fwd, to_device, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    import exact_attention_tiled_amd as eat
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    eat.load()
+
+
+def run_bwd(w, t, out, lse, **kw):
+    import exact_attention_tiled_amd as eat
+    return eat.attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], t["cu_q"], t["cu_k"],
+                        w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode, w.window, **kw)
+
+
+def _oracle_bwd(w, seqs=None, kv_heads=None):
+    return oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
+                                w.window, seqs=seqs, kv_heads=kv_heads)
+
+
+def check_grads(w, got, ref, what):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert_close(to_np(g), r, *BF16_TOL, f"{what} {name}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,window", [(1, 0), (2, 0), (0, 0), (1, 70), (2, 33)])
+def test_bwd_ragged_edges(d, mode, window):
+    """Ragged lengths around tile edges (incl. 0, 1, Nq > Nk and Nq < Nk), GQA 4:2."""
+    lq = [0, 1, 63, 64, 65, 127, 128, 129, 200, 7]
+    lk = [5, 129, 128, 64, 63, 1, 300, 129, 0, 70]
+    w = wl.random_workload((21, d, mode), lq, lk, 4, 2, d, "bf16", mode, window,
+                           with_dout=True, v_offsets=True, name="bwd-edge")
+    print(f"bwd edges d={d} mode={mode} window={window}", flush=True)
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    got = run_bwd(w, t, out, lse)
+    check_grads(w, got, _oracle_bwd(w), f"edges d={d} mode={mode} w={window}")
+
+
+def test_bwd_gqa_groups_are_summed():
+    """Hq=8 over Hkv=2: dK/dV of each K/V head equal the sum over its 4 query heads, checked
+    against the oracle's repeated-head (MHA) gradients summed per group."""
+    lens = [150, 77]
+    w = wl.random_workload(22, lens, lens, 8, 2, 128, "bf16", wl.MASK_CAUSAL_TOP_LEFT,
+                           with_dout=True, name="bwd-gqa")
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    dq, dk, dv = run_bwd(w, t, out, lse)
+    rq, rk, rv = oracle.attention_bwd(w.q, np.repeat(w.k, 4, axis=1), np.repeat(w.v, 4, axis=1),
+                                      w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode, 0)
+    assert_close(to_np(dk), rk.reshape(rk.shape[0], 2, 4, -1).sum(axis=2), *BF16_TOL, "gqa dK")
+    assert_close(to_np(dv), rv.reshape(rv.shape[0], 2, 4, -1).sum(axis=2), *BF16_TOL, "gqa dV")
+    assert_close(to_np(dq), rq, *BF16_TOL, "gqa dQ")
+
+
+def test_bwd_canaries_no_out_of_bounds_writes():
+    """Gradients land inside larger buffers whose slack holds sentinels: every sentinel
+    survives, and keys no query can see get exactly zero dK/dV ("Causal Mask and Ragged
+    Sequence Layouts", sixth section: a gradient written into a neighbouring packed
+    sequence goes unnoticed by forward-only tests)."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    lq, lk = [40, 3, 90], [10, 200, 90]
+    w = wl.random_workload(23, lq, lk, 4, 1, 64, "bf16", wl.MASK_CAUSAL_BOTTOM_RIGHT, 16,
+                           with_dout=True, name="canary")
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    pad = 4096
+    sentinel = -12345.0
+
+    def padded(like):
+        buf = torch.full((like.numel() + 2 * pad,), sentinel, dtype=like.dtype, device=like.device)
+        return buf, buf[pad:pad + like.numel()].view(like.shape)
+
+    bq, dq = padded(t["q"])
+    bk, dk = padded(t["k"])
+    bv, dv = padded(t["v"])
+    eat.attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], t["cu_q"], t["cu_k"],
+                 w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode, w.window, dq=dq, dk=dk,
+                 dv=dv)
+    torch.cuda.synchronize()
+    for buf in (bq, bk, bv):
+        assert torch.all(buf[:pad] == sentinel) and torch.all(buf[-pad:] == sentinel)
+    m = oracle.explicit_mask(w.cu_q, w.cu_k, w.mask_mode, w.window)
+    unseen = np.nonzero(~m.any(axis=0))[0]
+    assert len(unseen) > 50
+    assert torch.all(dk[torch.from_numpy(unseen).cuda()].float() == 0)
+    assert torch.all(dv[torch.from_numpy(unseen).cuda()].float() == 0)
+    check_grads(w, (dq, dk, dv), _oracle_bwd(w), "canary")
+
+
+@pytest.mark.parametrize("window", [0, 1024])
+def test_train_full_size(window):
+    """B=2, Hq=32, Hkv=8, N=8192, d=128, causal top-left (and window 1024): full GPU
+    forward + backward; oracle on one (sequence, K/V head group) slice: O, LSE of its 4
+    query heads and dQ, dK, dV of the whole group."""
+    w = wl.train_bf16(window=window)
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    dq, dk, dv = run_bwd(w, t, out, lse)
+    o, l = to_np(out), to_np(lse)
+    gq, gk, gv = to_np(dq), to_np(dk), to_np(dv)
+    for x in (o, l, gq, gk, gv):
+        assert np.all(np.isfinite(x))
+    s, g = 1, 3
+    heads = list(range(4 * g, 4 * g + 4))
+    ref_o, ref_l = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode,
+                                    w.window, seqs=[s], heads=heads)
+    rq, rk, rv = _oracle_bwd(w, seqs=[s], kv_heads=[g])
+    rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+    assert_close(o[rows][:, heads], ref_o[rows][:, heads], *BF16_TOL, "train O")
+    assert_close(l[heads][:, rows], ref_l[heads][:, rows], 1e-3, 0.0, "train LSE")
+    assert_close(gq[rows][:, heads], rq[rows][:, heads], *BF16_TOL, "train dQ")
+    assert_close(gk[rows][:, g], rk[rows][:, g], *BF16_TOL, "train dK")
+    assert_close(gv[rows][:, g], rv[rows][:, g], *BF16_TOL, "train dV")

@@ -1,0 +1,265 @@
+"""GPU forward parity against the fp64 oracle (both forward paths), bit-exact mask checks."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import (BF16_TOL, F32_TOL, LSE_TOL, assert_close, check_fwd, run_fwd, to_device,
+                      to_np)
+
+pytestmark = pytest.mark.gpu
+
+PREFILL, SPLITK = 1, 2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    import exact_attention_tiled_amd as eat
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    eat.load()
+
+
+def _oracle(w, seqs=None, heads=None):
+    return oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode, w.window,
+                            seqs=seqs, heads=heads)
+
+
+# ----------------------------------------------------------------------------------------
+# mask unit: bit-exact against the explicit mask from sequence ids and positions
+# ----------------------------------------------------------------------------------------
+
+MASK_PACKS = [
+    ([63, 64, 65], [63, 64, 65]),
+    ([127, 128, 129, 1, 0, 5], [127, 128, 129, 1, 3, 0]),
+    ([40, 300], [200, 100]),
+    ([257], [1]),
+    ([1, 2, 3], [300, 64, 129]),
+]
+
+
+@pytest.mark.parametrize("pack", range(len(MASK_PACKS)))
+@pytest.mark.parametrize("mode,window", [(0, 0), (1, 0), (2, 0), (1, 1), (1, 64), (2, 7), (2, 130)])
+def test_mask_probe_bit_exact(pack, mode, window):
+    import torch
+    import exact_attention_tiled_amd as eat
+    lq, lk = MASK_PACKS[pack]
+    cu_q, cu_k = wl.cu_from_lengths(lq), wl.cu_from_lengths(lk)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    print(f"mask probe pack={pack} mode={mode} window={window}", flush=True)
+    bits = eat.attn_mask_probe(torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda(),
+                               tq, tk, mode, window, 0, tq, 0, tk)
+    got = bits.cpu().numpy().astype(bool)
+    want = oracle.explicit_mask(cu_q, cu_k, mode, window)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:10].tolist()
+
+
+# ----------------------------------------------------------------------------------------
+# tiny fp32 workload (B=2, H=2, N=128, d=64), bottom-right and no mask
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [wl.MASK_CAUSAL_BOTTOM_RIGHT, wl.MASK_NONE])
+@pytest.mark.parametrize("path", [0, PREFILL])
+def test_tiny_f32(mode, path):
+    w = wl.tiny_f32(mode)
+    print(f"tiny_f32 mode={mode} path={path}", flush=True)
+    ref_o, ref_l = _oracle(w)
+    out, lse = run_fwd(w, path=path)
+    check_fwd(w, out, lse, ref_o, ref_l, f"tiny f32 mode {mode} path {path}")
+
+
+# ----------------------------------------------------------------------------------------
+# ragged edge lengths around tile boundaries, both dtypes, all alignments, GQA, both paths
+# ----------------------------------------------------------------------------------------
+
+EDGE = [0, 1, 63, 64, 65, 127, 128, 129]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,window", [(0, 0), (1, 0), (2, 0), (1, 50), (2, 97)])
+def test_edge_lengths_prefill(dtype, d, mode, window):
+    lq = EDGE + [5, 200]
+    lk = EDGE[::-1] + [300, 3]
+    w = wl.random_workload((11, d, mode), lq, lk, 4, 2, d, dtype, mode, window, name="edge",
+                           v_offsets=True)
+    print(f"edge prefill dtype={dtype} d={d} mode={mode} window={window}", flush=True)
+    ref_o, ref_l = _oracle(w)
+    out, lse = run_fwd(w, path=PREFILL)
+    check_fwd(w, out, lse, ref_o, ref_l, "edge prefill")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,window", [(2, 0), (1, 0), (0, 0), (2, 300)])
+@pytest.mark.parametrize("nq,group", [(1, 4), (3, 8), (16, 4), (64, 1)])
+def test_splitk_decode_shapes(dtype, mode, window, nq, group):
+    lk = [1, 129, 700, 2048, 0, 333]
+    lq = [min(nq, x) if mode == 1 else nq for x in lk]
+    w = wl.random_workload((12, nq, mode), lq, lk, 2 * group, 2, 128, dtype, mode, window,
+                           name="decode-small", v_offsets=True)
+    print(f"splitk dtype={dtype} mode={mode} window={window} nq={nq} group={group}", flush=True)
+    ref_o, ref_l = _oracle(w)
+    for splits in (0, 1, 3):
+        out, lse = run_fwd(w, path=SPLITK, num_splits=splits)
+        check_fwd(w, out, lse, ref_o, ref_l, f"splitk splits={splits}")
+    out, lse = run_fwd(w, path=PREFILL)
+    check_fwd(w, out, lse, ref_o, ref_l, "same shapes via prefill")
+
+
+# ----------------------------------------------------------------------------------------
+# bit-exact behaviour: empty rows, masked K/V perturbation, packing, determinism
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", [PREFILL, SPLITK])
+def test_empty_rows_are_exact_zero(path):
+    """Nq = 64 > Nk = 32 under bottom-right alignment: the first 32 rows of every sequence
+    are empty -> O = +0.0 (all bits zero) and LSE = -inf exactly."""
+    if path == PREFILL:
+        w = wl.decode(64, nk=32)            # the full Nq = 64 > Nk = 32 edge workload
+        n_empty = 32
+    else:                                   # split-K holds at most 64 rows per K/V head
+        w = wl.random_workload(16, [16] * 5, [8, 8, 1, 16, 9], 8, 2, 128, "bf16",
+                               wl.MASK_CAUSAL_BOTTOM_RIGHT, name="empty-rows-splitk")
+        n_empty = None
+    print(f"empty rows path={path}", flush=True)
+    out, lse = run_fwd(w, path=path)
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    for s in range(w.num_seqs):
+        lq, lk = int(w.cu_q[s + 1] - w.cu_q[s]), int(w.cu_k[s + 1] - w.cu_k[s])
+        ne = n_empty if n_empty is not None else max(0, lq - lk)
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s]) + ne)
+        assert np.all(o[rows].view(np.uint32) == 0), "empty rows must be +0.0"
+        assert np.all(l[:, rows] == -np.inf)
+        assert np.all(np.isfinite(l[:, int(w.cu_q[s]) + ne:int(w.cu_q[s + 1])]))
+    ref_o, ref_l = _oracle(w)
+    check_fwd(w, out, lse, ref_o, ref_l, "edge decode")
+
+
+@pytest.mark.parametrize("path", [PREFILL, SPLITK])
+def test_masked_kv_changes_nothing(path):
+    """Overwriting K/V entries no query may see (other sequences' neighbours, future keys,
+    keys beyond the window) with large finite values leaves every output bit unchanged."""
+    import torch
+    lq, lk = [100, 1, 50, 7], [130, 200, 50, 1500]
+    w = wl.random_workload(13, lq, lk, 4, 2, 128, "bf16", wl.MASK_CAUSAL_BOTTOM_RIGHT, 64,
+                           name="perturb")
+    t = to_device(w)
+    if path == SPLITK:
+        w = wl.random_workload(13, [3, 1, 2, 7], lk, 4, 2, 128, "bf16",
+                               wl.MASK_CAUSAL_BOTTOM_RIGHT, 64, name="perturb")
+        t = to_device(w)
+    out1, lse1 = run_fwd(w, t, path=path)
+    m = oracle.explicit_mask(w.cu_q, w.cu_k, w.mask_mode, w.window)
+    unseen = ~m.any(axis=0)
+    assert unseen.sum() > 100
+    k2, v2 = t["k"].clone(), t["v"].clone()
+    idx = torch.from_numpy(np.nonzero(unseen)[0]).cuda()
+    k2[idx] = 1.0e4
+    v2[idx] = -3.0e4
+    t2 = dict(t, k=k2, v=v2)
+    out2, lse2 = run_fwd(w, t2, path=path)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_packing_order_is_bitwise_neutral():
+    """Each sequence's forward result is bitwise independent of where it sits in the pack
+    (tiles start at each sequence's first token)."""
+    import torch
+    lens = [70, 129, 5, 300]
+    w = wl.random_workload(14, lens, lens, 4, 4, 128, "bf16", wl.MASK_CAUSAL_TOP_LEFT,
+                           name="pack")
+    out, lse = run_fwd(w, path=PREFILL)
+    perm = [2, 0, 3, 1]
+    cu = w.cu_q
+    q = np.concatenate([w.q[cu[s]:cu[s + 1]] for s in perm])
+    k = np.concatenate([w.k[cu[s]:cu[s + 1]] for s in perm])
+    v = np.concatenate([w.v[cu[s]:cu[s + 1]] for s in perm])
+    lp = [lens[s] for s in perm]
+    w2 = wl.Workload("pack2", "bf16", q, k, v, wl.cu_from_lengths(lp), wl.cu_from_lengths(lp),
+                     w.scale, w.mask_mode)
+    out2, lse2 = run_fwd(w2, path=PREFILL)
+    cu2 = w2.cu_q
+    for j, s in enumerate(perm):
+        a = out[cu[s]:cu[s + 1]].view(torch.int16)
+        b = out2[cu2[j]:cu2[j + 1]].view(torch.int16)
+        assert torch.equal(a, b), f"sequence {s}"
+        assert torch.equal(lse[:, cu[s]:cu[s + 1]].contiguous().view(torch.int32),
+                           lse2[:, cu2[j]:cu2[j + 1]].contiguous().view(torch.int32))
+
+
+def test_forward_is_deterministic():
+    import torch
+    w = wl.dense_bf16(batch=2, seqlen=1024, heads=4)
+    t = to_device(w)
+    a = run_fwd(w, t)
+    b = run_fwd(w, t)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_unusual_scales(scale):
+    w = wl.random_workload(15, [7, 20], [90, 150], 2, 1, 64, "f32", wl.MASK_CAUSAL_BOTTOM_RIGHT,
+                           name="scale", scale=scale)
+    ref_o, ref_l = _oracle(w)
+    for path in (PREFILL, SPLITK):
+        out, lse = run_fwd(w, path=path)
+        check_fwd(w, out, lse, ref_o, ref_l, f"scale {scale} path {path}")
+
+
+# ----------------------------------------------------------------------------------------
+# the named workloads at full size (oracle on sampled sequences / heads)
+# ----------------------------------------------------------------------------------------
+
+def test_dense_bf16_full_size():
+    """B=4, H=16, N=2048, d=128, causal top-left; oracle on 3 (sequence, head) slices."""
+    w = wl.dense_bf16()
+    out, lse = run_fwd(w)
+    o, l = to_np(out), to_np(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    for s, h in ((0, 0), (2, 7), (3, 15)):
+        ref_o, ref_l = _oracle(w, seqs=[s], heads=[h])
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+        assert_close(o[rows, h], ref_o[rows, h], *BF16_TOL, f"dense O s{s} h{h}")
+        assert_close(l[h, rows], ref_l[h, rows], LSE_TOL, 0.0, f"dense LSE s{s} h{h}")
+
+
+def test_ragged_gqa_full_size():
+    """16384 packed tokens, ragged lengths incl. 63/64/65/127/128/129, Hq=32, Hkv=8; oracle
+    on every short sequence and on the longest, over heads spanning several GQA groups."""
+    w = wl.ragged_gqa()
+    out, lse = run_fwd(w)
+    o, l = to_np(out), to_np(lse)
+    assert np.all(np.isfinite(o))
+    lens = np.diff(w.cu_q)
+    seqs = [int(s) for s in np.nonzero(lens <= 129)[0]] + [int(np.argmax(lens))]
+    heads = [0, 3, 4, 13, 31]
+    ref_o, ref_l = _oracle(w, seqs=seqs, heads=heads)
+    for s in seqs:
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+        for h in heads:
+            assert_close(o[rows, h], ref_o[rows, h], *BF16_TOL, f"ragged O s{s} h{h}")
+            assert_close(l[h, rows], ref_l[h, rows], LSE_TOL, 0.0, f"ragged LSE s{s} h{h}")
+
+
+@pytest.mark.parametrize("nq", [1, 4, 16])
+def test_decode_full_size(nq):
+    """B=16, Hq=32, Hkv=8, d=128, Nk=32768, bottom-right; oracle on 3 (sequence, K/V head)
+    groups; the auto plan must pick the split-K path."""
+    import exact_attention_tiled_amd as eat
+    w = wl.decode(nq)
+    t = to_device(w)
+    plan = eat.attn_describe_plan(t["q"], t["k"], t["cu_q"], w.max_seqlen_q, w.max_seqlen_k,
+                                  w.mask_mode)
+    assert plan.startswith("path=splitk"), plan
+    out, lse = run_fwd(w, t)
+    o, l = to_np(out), to_np(lse)
+    del t
+    for s, g in ((0, 0), (7, 5), (15, 7)):
+        heads = list(range(4 * g, 4 * g + 4))
+        ref_o, ref_l = _oracle(w, seqs=[s], heads=heads)
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+        assert_close(o[rows][:, heads], ref_o[rows][:, heads], *BF16_TOL, f"decode O s{s} g{g}")
+        assert_close(l[heads][:, rows], ref_l[heads][:, rows], LSE_TOL, 0.0, f"decode LSE s{s}")
