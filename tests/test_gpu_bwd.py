@@ -29,8 +29,10 @@ def _oracle_bwd(w, seqs=None, kv_heads=None):
 
 
 def check_grads(w, got, ref, what):
+    worst = {}
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        assert_close(to_np(g), r, *BF16_TOL, f"{what} {name}")
+        worst[name] = assert_close(to_np(g), r, *BF16_TOL, f"{what} {name}")
+    print(f"{what}: max abs errors {worst}", flush=True)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -39,8 +41,11 @@ def test_bwd_ragged_edges(d, mode, window):
     """Ragged lengths around tile edges (incl. 0, 1, Nq > Nk and Nq < Nk), GQA 4:2."""
     lq = [0, 1, 63, 64, 65, 127, 128, 129, 200, 7]
     lk = [5, 129, 128, 64, 63, 1, 300, 129, 0, 70]
+    # N(0,1) values as in the training workload. Large per-sequence value offsets (used by
+    # the forward tests to expose leaks) do not suit the backward: D = rowsum(dO * O) is
+    # formed from the stored bf16 output, whose spacing near |O| = 90 is 0.5.
     w = wl.random_workload((21, d, mode), lq, lk, 4, 2, d, "bf16", mode, window,
-                           with_dout=True, v_offsets=True, name="bwd-edge")
+                           with_dout=True, name="bwd-edge")
     print(f"bwd edges d={d} mode={mode} window={window}", flush=True)
     t = to_device(w)
     out, lse = run_fwd(w, t)
