@@ -43,10 +43,11 @@ int validate_common(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t 
 // Path choice. Split-K when the query rows of one K/V head fit one wave's two 32-row
 // blocks and the key range is long enough to be worth splitting; prefill otherwise.
 int make_plan(int32_t num_seqs, int32_t total_q, int32_t max_q, int32_t max_k, int32_t hq,
-              int32_t hkv, int32_t d, int32_t path, int32_t num_splits, Plan* plan) {
+              int32_t hkv, int32_t d, int32_t dtype, int32_t path, int32_t num_splits, Plan* plan) {
   const int group = hq / hkv;
   const long rows = (long)group * max_q;
-  const bool splitk_ok = rows <= attn::SPLITK_MAX_ROWS;
+  // Two 128-key fp32 stages of head_dim 128 exceed the 160 KiB of LDS.
+  const bool splitk_ok = rows <= attn::SPLITK_MAX_ROWS && !(dtype == ATTN_F32 && d == 128);
   if (path == ATTN_PATH_AUTO) path = (splitk_ok && max_k >= 1024) ? ATTN_PATH_SPLITK : ATTN_PATH_PREFILL;
   if (path != ATTN_PATH_PREFILL && path != ATTN_PATH_SPLITK) return ATTN_ERR_BAD_PLAN;
   if (num_splits < 0) return ATTN_ERR_BAD_PLAN;
@@ -152,7 +153,7 @@ size_t attn_fwd_ex_workspace_size(int32_t num_seqs, int32_t total_q, int32_t tot
                       window) != ATTN_OK)
     return 0;
   Plan plan;
-  if (make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, path, num_splits, &plan) != ATTN_OK)
+  if (make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits, &plan) != ATTN_OK)
     return 0;
   return plan.workspace;
 }
@@ -174,7 +175,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_q
   if (rc != ATTN_OK) return rc;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   Plan plan;
-  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, path, num_splits, &plan);
+  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits, &plan);
   if (rc != ATTN_OK) return rc;
   if (num_seqs == 0 || total_q == 0) return ATTN_OK;
   if (!cu_q || !cu_k || !out || !lse || !q) return ATTN_ERR_NULL_PTR;
@@ -269,7 +270,7 @@ int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32
                            window);
   if (rc != ATTN_OK) return rc;
   Plan plan;
-  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, path, num_splits, &plan);
+  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits, &plan);
   if (rc != ATTN_OK) return rc;
   if (!buf || len == 0) return ATTN_ERR_NULL_PTR;
   const char* dt = dtype == ATTN_BF16 ? "bf16" : "f32";

@@ -26,6 +26,36 @@ namespace attn {
 constexpr int BWD_BN = 128;  // keys per workgroup
 constexpr int BWD_BM = 64;   // queries per iteration
 
+// Register-staged tile copy: global -> registers -> LDS (padded rows), 16 bytes per access.
+// Rows at or beyond `valid_rows` are zero-filled and never read from memory.
+template <int ROW_BYTES, int ROWS, int NTHREADS>
+struct RowStager {
+  static constexpr int CHUNKS = ROW_BYTES / 16;
+  static constexpr int TOTAL = ROWS * CHUNKS;
+  static_assert(TOTAL % NTHREADS == 0, "tile must split evenly over the threads");
+  static constexpr int PER_THREAD = TOTAL / NTHREADS;
+  i32x4 r[PER_THREAD];
+
+  __device__ __forceinline__ void load(const char* base, size_t row_stride_bytes, int valid_rows,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int idx = i * NTHREADS + tid;
+      const int row = idx / CHUNKS, c = idx % CHUNKS;
+      r[i] = row < valid_rows ? *reinterpret_cast<const i32x4*>(base + row * row_stride_bytes + c * 16)
+                              : i32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int pitch, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int idx = i * NTHREADS + tid;
+      const int row = idx / CHUNKS, c = idx % CHUNKS;
+      *reinterpret_cast<i32x4*>(lds + row * pitch + c * 16) = r[i];
+    }
+  }
+};
+
 struct BwdParams {
   const __bf16* q;
   const __bf16* k;
@@ -107,7 +137,7 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __rest
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   typedef Mma<__bf16, D> M;
-  constexpr int PITCH = M::PITCH;                 // Q, dO, K rows: D bf16 + 16 bytes
+  constexpr int PITCH = D * 2 + 16;               // Q, dO, K rows: D bf16 + 16 bytes
   constexpr int SPITCH = BWD_BN * 2 + 16;         // dS rows: 128 keys bf16 + 16 bytes
   constexpr int NDB = D / 32;
   constexpr int QREGS = D / 16;

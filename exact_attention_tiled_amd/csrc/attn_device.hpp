@@ -58,14 +58,32 @@ struct SeqGeom {
   int off;
 };
 
-__device__ __forceinline__ SeqGeom load_geom(const int32_t* cu_q, const int32_t* cu_k, int s,
-                                             int mode) {
+// Values the whole workgroup shares but the compiler cannot prove uniform (they come from
+// vector loads of cu_seqlens). Marking them uniform keeps address and descriptor
+// arithmetic in scalar registers.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Geometry of sequence s, which may differ from lane to lane.
+__device__ __forceinline__ SeqGeom load_geom_lane(const int32_t* cu_q, const int32_t* cu_k, int s,
+                                                  int mode) {
   SeqGeom g;
   g.q_start = cu_q[s];
   g.k_start = cu_k[s];
   g.len_q = cu_q[s + 1] - g.q_start;
   g.len_k = cu_k[s + 1] - g.k_start;
   g.off = (mode == MASK_BOTTOM_RIGHT) ? g.len_k - g.len_q : 0;
+  return g;
+}
+
+// Geometry of sequence s when s is the same for the whole workgroup.
+__device__ __forceinline__ SeqGeom load_geom(const int32_t* cu_q, const int32_t* cu_k, int s,
+                                             int mode) {
+  SeqGeom g = load_geom_lane(cu_q, cu_k, s, mode);
+  g.q_start = uniform(g.q_start);
+  g.k_start = uniform(g.k_start);
+  g.len_q = uniform(g.len_q);
+  g.len_k = uniform(g.len_k);
+  g.off = uniform(g.off);
   return g;
 }
 
@@ -131,9 +149,9 @@ __device__ __forceinline__ int seq_of_slot(const int32_t* cu_q, int num_seqs, in
   int lo = 0, hi = num_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (cu_q[mid] / BM + mid <= slot) lo = mid; else hi = mid - 1;
+    if (uniform(cu_q[mid]) / BM + mid <= slot) lo = mid; else hi = mid - 1;
   }
-  return lo;
+  return uniform(lo);
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8). This maps
@@ -147,44 +165,72 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nlogical) {
 }
 
 // ---------------------------------------------------------------------------------------
-// K/V staging: global -> registers -> LDS, 16 bytes per access. Rows at or beyond
-// `valid_rows` are zero-filled and never read from memory (no access past the sequence's
-// last key, so nothing past the end of the tensor either).
+// Swizzled LDS tiles filled by buffer -> LDS DMA.
+//
+// A tile row r of ROWB bytes occupies [r * ROWB, (r + 1) * ROWB) with its 16-byte chunk c
+// stored at slot c ^ (r & 7). The XOR spreads the same chunk of 8 consecutive rows over 8
+// different bank groups, so the column-wise MFMA operand reads are conflict-free without
+// padding (padding cannot be used: one DMA instruction writes 64 lanes x 16 bytes
+// contiguously).
+//
+// buffer_load_dwordx4 ... lds writes lane l's 16 bytes to LDS at (wave-uniform base) +
+// 16 l. Lane l of instruction i therefore fetches the global chunk that belongs at its
+// fixed LDS slot. The buffer descriptor covers only the tile's valid rows, so rows past
+// the sequence end (or the tensor end) are never read: the hardware range check returns
+// zeros for them.
 // ---------------------------------------------------------------------------------------
-template <int ROW_BYTES, int ROWS, int NTHREADS>
-struct RowStager {
-  static constexpr int CHUNKS = ROW_BYTES / 16;
-  static constexpr int TOTAL = ROWS * CHUNKS;
-  static_assert(TOTAL % NTHREADS == 0, "tile must split evenly over the threads");
-  static constexpr int PER_THREAD = TOTAL / NTHREADS;
-  i32x4 r[PER_THREAD];
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ (row & 7); }
 
-  __device__ __forceinline__ void load(const char* base, size_t row_stride_bytes, int valid_rows,
-                                       int tid) {
+template <int ROWB, int ROWS, int NWAVES>
+struct DmaStager {
+  static constexpr int C = ROWB / 16;        // chunks per row
+  static constexpr int RPI = 1024 / ROWB;    // rows per DMA instruction
+  static constexpr int NINST = ROWS / RPI;   // instructions per tile
+  static_assert(C >= 8 && NINST % NWAVES == 0, "tile shape");
+  static constexpr int PER_WAVE = NINST / NWAVES;
+  uint32_t voff[PER_WAVE];
+  int first_row;
+
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_stride) {
+    first_row = wave * PER_WAVE * RPI;
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int idx = i * NTHREADS + tid;
-      const int row = idx / CHUNKS, c = idx % CHUNKS;
-      if (row < valid_rows) {
-        r[i] = *reinterpret_cast<const i32x4*>(base + row * row_stride_bytes + c * 16);
-      } else {
-        r[i] = i32x4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int row = first_row + i * RPI + lane / C;
+      voff[i] = (uint32_t)row * row_stride + (uint32_t)(swz_chunk(row, lane % C) << 4);
     }
   }
-  __device__ __forceinline__ void store(char* lds, int pitch, int tid) const {
+  // Rows [0, valid_rows) of the tile start at `rows` (global) with stride `row_stride`.
+  __device__ __forceinline__ void issue(const char* rows, int valid_rows, uint32_t row_stride,
+                                        char* lds_tile) const {
+    // The buffer descriptor type exists only for the GPU target; the host pass never runs
+    // this body and must not see it (it would drop kernel launch stubs).
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int v = valid_rows < 0 ? 0 : (valid_rows > ROWS ? ROWS : valid_rows);
+    // The descriptor must live in scalar registers: every operand is workgroup-uniform.
+    const uint64_t base = (uint64_t)rows;
+    const uint64_t ubase = ((uint64_t)(uint32_t)uniform((int)(base >> 32)) << 32) |
+                           (uint32_t)uniform((int)(uint32_t)base);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(ubase), (short)0, uniform((int)((uint32_t)v * row_stride)),
+        0x00020000);
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int idx = i * NTHREADS + tid;
-      const int row = idx / CHUNKS, c = idx % CHUNKS;
-      *reinterpret_cast<i32x4*>(lds + row * pitch + c * 16) = r[i];
+    for (int i = 0; i < PER_WAVE; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (first_row + i * RPI) * ROWB),
+          16, voff[i], 0, 0, 0);
     }
+#endif
   }
 };
 
+// Wait for this thread's outstanding DMA / global loads (before the barrier that
+// publishes an LDS stage).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------------------------------
-// Element-type specific contractions. Key k of a 32-key block sits in register r of lane
-// half g = l / 32 with k = 8 * (r / 4) + 4 * g + (r % 4) (the accumulator layout above).
+// Element-type specific contractions on swizzled tiles. Key k of a 32-key block sits in
+// register r of lane half g = l / 32 with k = 8 * (r / 4) + 4 * g + (r % 4) (the
+// accumulator layout above).
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int key_of_reg(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
@@ -194,9 +240,30 @@ struct Mma;
 // bf16: v_mfma_f32_32x32x16_bf16 for both contractions; V^T operands via ds_read_b64_tr_b16.
 template <int D>
 struct Mma<__bf16, D> {
-  static constexpr int PITCH = D * 2 + 16;  // LDS row pitch (bytes): +16 spreads rows over banks
+  static constexpr int ROWB = D * 2;
   static constexpr int QREGS = D / 16;
+  static constexpr int NDB = D / 32;
   typedef bf16x8 QOperand;
+
+  // Per-lane LDS byte offsets, fixed for the whole kernel.
+  struct Offsets {
+    int k[QREGS];   // K operand of step s: row l % 32, chunk 2 s + l / 32
+    int v[NDB];     // V^T operand of head-dim block db (row part 4 g + (l % 16) / 4)
+  };
+  __device__ static Offsets offsets(int lane) {
+    Offsets o;
+    const int i = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < QREGS; ++s) o.k[s] = i * ROWB + (swz_chunk(i, 2 * s + g) << 4);
+    const int a16 = lane & 15, hh = (lane >> 4) & 1;
+    const int x = 4 * g + (a16 >> 2);  // row within an aligned group of 8
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int c = 4 * db + 2 * hh + ((a16 & 3) >> 1);
+      o.v[db] = x * ROWB + (swz_chunk(x, c) << 4) + 8 * (a16 & 1);
+    }
+    return o;
+  }
 
   // Q^T operand of S^T = K Q^T: lane (q = l % 32, g = l / 32) holds q[16 s + 8 g + 0..7].
   // `neg` flips the sign bit (exact) so a negative scale becomes a positive one.
@@ -211,12 +278,13 @@ struct Mma<__bf16, D> {
     }
   }
 
-  // acc += K_block Q^T over the full head dimension; kl points at LDS row 0 of the block.
-  __device__ static void qk(f32x16& acc, const char* kl, const QOperand (&qr)[QREGS], int lane) {
-    const char* p = kl + (lane & 31) * PITCH + (lane >> 5) * 16;
+  // acc += K_block Q^T over the full head dimension; kl points at tile row 0 of the block
+  // (a multiple of 8 rows into the tile).
+  __device__ static void qk(f32x16& acc, const char* kl, const QOperand (&qr)[QREGS],
+                            const Offsets& of, int lane) {
 #pragma unroll
     for (int s = 0; s < QREGS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(p + s * 32);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + of.k[s]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[s], acc, 0, 0, 0);
     }
   }
@@ -224,22 +292,21 @@ struct Mma<__bf16, D> {
   // o[db] += V_block^T P^T for the 32 keys of one block; p holds P^T in accumulator layout.
   // K-slot t = 4 j + u of step s carries key 16 s + 8 j + 4 g + u, which is register
   // 8 s + t of p, and is what the two transpose reads (rows +0 and +8) return.
-  __device__ static void pv(f32x16 (&o)[D / 32], const f32x16& p, const char* vl, int lane) {
+  __device__ static void pv(f32x16 (&o)[NDB], const f32x16& p, const char* vl, const Offsets& of,
+                            int lane) {
     bf16x8 b[2];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       b[0][t] = (__bf16)p[t];
       b[1][t] = (__bf16)p[8 + t];
     }
-    const int a16 = lane & 15, hh = (lane >> 4) & 1, g = lane >> 5;
-    const char* base = vl + (4 * g + (a16 >> 2)) * PITCH + (16 * hh + 4 * (a16 & 3)) * 2;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const char* p0 = base + 16 * s * PITCH + db * 64;
+        const char* p0 = vl + 16 * s * ROWB + of.v[db];
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * PITCH));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * ROWB));
         const i32x4 cat = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
                            __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), b[s],
@@ -259,9 +326,12 @@ struct Mma<__bf16, D> {
 // fp32: v_mfma_f32_32x32x2_f32 (exact products, fp32 accumulation).
 template <int D>
 struct Mma<float, D> {
-  static constexpr int PITCH = D * 4 + 16;
+  static constexpr int ROWB = D * 4;
   static constexpr int QREGS = D / 2;
+  static constexpr int NDB = D / 32;
   typedef float QOperand;
+  struct Offsets {};
+  __device__ static Offsets offsets(int) { return Offsets{}; }
 
   __device__ static void load_q(QOperand (&qr)[QREGS], const float* qrow, bool valid, bool neg,
                                 int lane) {
@@ -273,23 +343,28 @@ struct Mma<float, D> {
     }
   }
 
-  __device__ static void qk(f32x16& acc, const char* kl, const QOperand (&qr)[QREGS], int lane) {
-    const float* p = reinterpret_cast<const float*>(kl + (lane & 31) * PITCH) + (lane >> 5);
+  // Element e of row r lives at r * ROWB + (swz(r, e / 4) << 4) + 4 (e % 4).
+  __device__ static int at(int row, int e) { return row * ROWB + (swz_chunk(row, e >> 2) << 4) + 4 * (e & 3); }
+
+  __device__ static void qk(f32x16& acc, const char* kl, const QOperand (&qr)[QREGS], const Offsets&,
+                            int lane) {
+    const int i = lane & 31, g = lane >> 5;
 #pragma unroll
     for (int s = 0; s < QREGS; ++s) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(p[2 * s], qr[s], acc, 0, 0, 0);
+      const float a = *reinterpret_cast<const float*>(kl + at(i, 2 * s + g));
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qr[s], acc, 0, 0, 0);
     }
   }
 
   // Step r contracts the two keys held in register r by the two lane halves.
-  __device__ static void pv(f32x16 (&o)[D / 32], const f32x16& p, const char* vl, int lane) {
+  __device__ static void pv(f32x16 (&o)[NDB], const f32x16& p, const char* vl, const Offsets&,
+                            int lane) {
     const int i = lane & 31, g = lane >> 5;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float a =
-            *reinterpret_cast<const float*>(vl + key_of_reg(r, g) * PITCH + (db * 32 + i) * 4);
+        const float a = *reinterpret_cast<const float*>(vl + at(key_of_reg(r, g), db * 32 + i));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[r], o[db], 0, 0, 0);
       }
     }

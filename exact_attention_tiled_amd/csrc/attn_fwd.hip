@@ -81,17 +81,54 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], bool need_mask, in
   }
 }
 
+// Running state of one prefill wave (32 query rows) and its step over one 64-key stage.
+template <typename T, int D>
+struct PrefillWave {
+  typedef Mma<T, D> M;
+  f32x16 o[D / 32];
+  float m_run, l_run;
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    m_run = neg_inf();
+    l_run = 0.0f;
+  }
+
+  // One stage of FWD_BN keys starting at key position k0, staged at `buf` (K tile, then
+  // V tile). The wave's rows are query positions [wp0, wp1); this lane's query is pq.
+  __device__ __forceinline__ void stage(const char* buf, int k0, int wp0, int wp1, int pq,
+                                        const SeqGeom& g, const FwdParams& p,
+                                        const typename M::QOperand (&qr)[M::QREGS],
+                                        const typename M::Offsets& of, int lane) {
+    constexpr int ROWB = M::ROWB, TILE = FWD_BN * ROWB;
+    const int cls = block_class(wp0, wp1, k0, k0 + FWD_BN, g, p.mode, p.window);
+    if (cls == 0) return;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+      M::qk(sacc[kb], buf + kb * 32 * ROWB, qr, of, lane);
+    }
+    softmax_step<2, D>(sacc, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run, l_run, o, lane);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) M::pv(o, sacc[kb], buf + TILE + kb * 32 * ROWB, of, lane);
+  }
+};
+
 // ---------------------------------------------------------------------------------------
 // Prefill: one workgroup = 4 waves = 128 query rows of one (sequence, query head); all
-// waves share each 64-key K/V stage through a double-buffered LDS ring.
+// waves share each 64-key K/V stage. Stages are DMA'd into two LDS buffers in turn: the
+// load of stage j+1 is in flight while stage j is computed.
 // ---------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   typedef Mma<T, D> M;
-  constexpr int BM = FWD_BM, BN = FWD_BN, PITCH = M::PITCH;
-  constexpr int TILE = BN * PITCH;
-  constexpr int NSTAGE = (2 * 2 * TILE <= LDS_BYTES) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * 2 * TILE];
+  constexpr int BM = FWD_BM, BN = FWD_BN, ROWB = M::ROWB;
+  constexpr int TILE = BN * ROWB;
+  static_assert(2 * 2 * TILE <= LDS_BYTES, "two K/V stages must fit in LDS");
+  __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];  // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int w = xcd_logical_block(blockIdx.x, p.nlogical);
@@ -113,59 +150,49 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   typename M::QOperand qr[M::QREGS];
   const T* qrow = static_cast<const T*>(p.q) + ((size_t)(g.q_start + pq) * p.hq + h) * D;
   M::load_q(qr, qrow, qvalid, p.neg != 0, lane);
+  const typename M::Offsets of = M::offsets(lane);
 
   int klo, khi;
   visible_keys(p0, p1, g, p.mode, p.window, klo, khi);
   const int kstart = (klo / BN) * BN;
   const int nst = khi > klo ? (khi - kstart + BN - 1) / BN : 0;
 
-  typedef RowStager<D * (int)sizeof(T), BN, 256> Stager;
-  Stager sk, sv;
-  const size_t rstride = (size_t)p.hkv * D * sizeof(T);
+  const uint32_t rstride = (uint32_t)(p.hkv * D * sizeof(T));
   const char* kb0 = static_cast<const char*>(p.k) + ((size_t)g.k_start * p.hkv + kvh) * D * sizeof(T);
   const char* vb0 = static_cast<const char*>(p.v) + ((size_t)g.k_start * p.hkv + kvh) * D * sizeof(T);
+  DmaStager<ROWB, BN, 4> dma;
+  dma.init(wave, lane, rstride);
 
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m_run = neg_inf(), l_run = 0.0f;
+  PrefillWave<T, D> st;
+  st.init();
 
   if (nst > 0) {
-    sk.load(kb0 + kstart * rstride, rstride, min(BN, g.len_k - kstart), tid);
-    sv.load(vb0 + kstart * rstride, rstride, min(BN, g.len_k - kstart), tid);
-    sk.store(lds, PITCH, tid);
-    sv.store(lds + TILE, PITCH, tid);
+    dma.issue(kb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, buf0);
+    dma.issue(vb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, buf0 + TILE);
   }
+  wait_vmem();
   __syncthreads();
-  for (int it = 0; it < nst; ++it) {
+  for (int it = 0; it < nst; it += 2) {
     const int k0 = kstart + it * BN;
-    char* cur = lds + (NSTAGE == 2 ? (it & 1) : 0) * 2 * TILE;
-    char* nxt = lds + (NSTAGE == 2 ? ((it + 1) & 1) : 0) * 2 * TILE;
-    const bool more = it + 1 < nst;
-    if (more) {
-      const int kn = k0 + BN;
-      sk.load(kb0 + kn * rstride, rstride, min(BN, g.len_k - kn), tid);
-      sv.load(vb0 + kn * rstride, rstride, min(BN, g.len_k - kn), tid);
+    if (it + 1 < nst) {
+      dma.issue(kb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, buf1);
+      dma.issue(vb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, buf1 + TILE);
     }
-    const int cls = block_class(wp0, wp1, k0, k0 + BN, g, p.mode, p.window);
-    if (cls != 0) {
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        M::qk(sacc[kb], cur + kb * 32 * PITCH, qr, lane);
-      }
-      softmax_step<2, D>(sacc, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run, l_run, o, lane);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) M::pv(o, sacc[kb], cur + TILE + kb * 32 * PITCH, lane);
-    }
-    if (NSTAGE == 1) __syncthreads();  // single buffer: every wave is done reading it
-    if (more) {
-      sk.store(nxt, PITCH, tid);
-      sv.store(nxt + TILE, PITCH, tid);
-    }
+    st.stage(buf0, k0, wp0, wp1, pq, g, p, qr, of, lane);
+    wait_vmem();
     __syncthreads();
+    if (it + 1 < nst) {
+      if (it + 2 < nst) {
+        dma.issue(kb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, buf0);
+        dma.issue(vb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, buf0 + TILE);
+      }
+      st.stage(buf1, k0 + BN, wp0, wp1, pq, g, p, qr, of, lane);
+      wait_vmem();
+      __syncthreads();
+    }
   }
+  f32x16 (&o)[D / 32] = st.o;
+  const float m_run = st.m_run, l_run = st.l_run;
 
   // Epilogue: O = acc / l (exactly +0.0 for rows that saw no allowed key), natural-log LSE.
   const float lt = l_run + swap_halves(l_run);
@@ -189,6 +216,60 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   }
 }
 
+// Running state of one split-K wave (NRB blocks of 32 query rows) and its step over its
+// 32-key block of one 128-key stage.
+template <typename T, int D, int NRB>
+struct SplitkWave {
+  typedef Mma<T, D> M;
+  f32x16 o[NRB][D / 32];
+  float m_run[NRB], l_run[NRB];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[rb][db] = f32x16{};
+      m_run[rb] = neg_inf();
+      l_run[rb] = 0.0f;
+    }
+  }
+
+  __device__ __forceinline__ void stage(const char* buf, int k0, int klo, int khi, int R, int wave,
+                                        const int (&pq)[NRB], const SeqGeom& g,
+                                        const FwdParams& p,
+                                        const typename M::QOperand (&qr)[NRB][M::QREGS],
+                                        const typename M::Offsets& of, int lane) {
+    constexpr int ROWB = M::ROWB, TILE = SPLITK_STAGE * ROWB;
+    const int G = p.group;
+    const int kw = k0 + 32 * wave;  // this wave's key block
+    // A key outside this block's chunk belongs to a neighbouring chunk's partial.
+    const int cw0 = max(kw, klo), cw1 = min(kw + 32, khi);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int rlo = rb * 32, rhi = min(R, rb * 32 + 32);
+      const int cls = (rhi <= rlo || cw1 <= cw0)
+                          ? 0
+                          : block_class(rlo / G, (rhi - 1) / G + 1, kw, kw + 32, g, p.mode, p.window);
+      if (cls == 0) continue;
+      const bool clip = cw0 != kw || cw1 != kw + 32;
+      f32x16 sacc[1];
+      sacc[0] = f32x16{};
+      M::qk(sacc[0], buf + 32 * wave * ROWB, qr[rb], of, lane);
+      if (clip) {
+        const int hg = lane >> 5;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = kw + key_of_reg(r, hg);
+          sacc[0][r] = ((kk >= cw0) & (kk < cw1)) ? sacc[0][r] : neg_inf();
+        }
+      }
+      softmax_step<1, D>(sacc, cls == 1 || clip, pq[rb], kw, g, p.mode, p.window, p.c2,
+                         m_run[rb], l_run[rb], o[rb], lane);
+      M::pv(o[rb], sacc[0], buf + TILE + 32 * wave * ROWB, of, lane);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------------------
 // Split-K decode: one workgroup = one (sequence, K/V head, key chunk). Its rows are the
 // G * len_q (query head, query position) pairs of the group, shared by the 4 waves, so
@@ -199,10 +280,11 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
 template <typename T, int D, int NRB>
 __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
   typedef Mma<T, D> M;
-  constexpr int BN = SPLITK_STAGE, PITCH = M::PITCH;
-  constexpr int TILE = BN * PITCH;
-  constexpr int NSTAGE = (2 * 2 * TILE <= LDS_BYTES) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * 2 * TILE];
+  constexpr int BN = SPLITK_STAGE, ROWB = M::ROWB;
+  constexpr int TILE = BN * ROWB;
+  static_assert(2 * 2 * TILE <= LDS_BYTES, "two K/V stages must fit in LDS");
+  __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
@@ -227,6 +309,7 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
     const T* qrow = static_cast<const T*>(p.q) + ((size_t)(g.q_start + pq[rb]) * p.hq + h) * D;
     M::load_q(qr[rb], qrow, rvalid[rb], p.neg != 0, lane);
   }
+  const typename M::Offsets of = M::offsets(lane);
 
   int vlo, vhi;
   visible_keys(0, g.len_q, g, p.mode, p.window, vlo, vhi);
@@ -235,73 +318,42 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
   const int kstart = (klo / BN) * BN;
   const int nst = khi > klo ? (khi - kstart + BN - 1) / BN : 0;
 
-  typedef RowStager<D * (int)sizeof(T), BN, 256> Stager;
-  Stager sk, sv;
-  const size_t rstride = (size_t)p.hkv * D * sizeof(T);
+  const uint32_t rstride = (uint32_t)(p.hkv * D * sizeof(T));
   const char* kb0 = static_cast<const char*>(p.k) + ((size_t)g.k_start * p.hkv + kvh) * D * sizeof(T);
   const char* vb0 = static_cast<const char*>(p.v) + ((size_t)g.k_start * p.hkv + kvh) * D * sizeof(T);
+  DmaStager<ROWB, BN, 4> dma;
+  dma.init(wave, lane, rstride);
 
-  f32x16 o[NRB][D / 32];
-  float m_run[NRB], l_run[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[rb][db] = f32x16{};
-    m_run[rb] = neg_inf();
-    l_run[rb] = 0.0f;
-  }
-
+  SplitkWave<T, D, NRB> st;
+  st.init();
   if (nst > 0) {
-    sk.load(kb0 + kstart * rstride, rstride, min(BN, g.len_k - kstart), tid);
-    sv.load(vb0 + kstart * rstride, rstride, min(BN, g.len_k - kstart), tid);
-    sk.store(lds, PITCH, tid);
-    sv.store(lds + TILE, PITCH, tid);
+    dma.issue(kb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, buf0);
+    dma.issue(vb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, buf0 + TILE);
   }
+  wait_vmem();
   __syncthreads();
-  for (int it = 0; it < nst; ++it) {
+  for (int it = 0; it < nst; it += 2) {
     const int k0 = kstart + it * BN;
-    char* cur = lds + (NSTAGE == 2 ? (it & 1) : 0) * 2 * TILE;
-    char* nxt = lds + (NSTAGE == 2 ? ((it + 1) & 1) : 0) * 2 * TILE;
-    const bool more = it + 1 < nst;
-    if (more) {
-      const int kn = k0 + BN;
-      sk.load(kb0 + kn * rstride, rstride, min(BN, g.len_k - kn), tid);
-      sv.load(vb0 + kn * rstride, rstride, min(BN, g.len_k - kn), tid);
+    if (it + 1 < nst) {
+      dma.issue(kb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, buf1);
+      dma.issue(vb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, buf1 + TILE);
     }
-    const int kw = k0 + 32 * wave;  // this wave's key block
-    // A key outside this block's chunk belongs to a neighbouring chunk's partial.
-    const int cw0 = max(kw, klo), cw1 = min(kw + 32, khi);
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int rlo = rb * 32, rhi = min(R, rb * 32 + 32);
-      const int cls = (rhi <= rlo || cw1 <= cw0)
-                          ? 0
-                          : block_class(rlo / G, (rhi - 1) / G + 1, kw, kw + 32, g, p.mode, p.window);
-      if (cls != 0) {
-        const bool partial = cls == 1 || cw0 != kw || cw1 != kw + 32;
-        f32x16 sacc[1];
-        sacc[0] = f32x16{};
-        M::qk(sacc[0], cur + 32 * wave * PITCH, qr[rb], lane);
-        if (partial && (cw0 != kw || cw1 != kw + 32)) {
-          const int hg = lane >> 5;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = kw + key_of_reg(r, hg);
-            sacc[0][r] = ((kk >= cw0) & (kk < cw1)) ? sacc[0][r] : neg_inf();
-          }
-        }
-        softmax_step<1, D>(sacc, partial, pq[rb], kw, g, p.mode, p.window, p.c2, m_run[rb],
-                           l_run[rb], o[rb], lane);
-        M::pv(o[rb], sacc[0], cur + TILE + 32 * wave * PITCH, lane);
-      }
-    }
-    if (NSTAGE == 1) __syncthreads();  // single buffer: every wave is done reading it
-    if (more) {
-      sk.store(nxt, PITCH, tid);
-      sv.store(nxt + TILE, PITCH, tid);
-    }
+    st.stage(buf0, k0, klo, khi, R, wave, pq, g, p, qr, of, lane);
+    wait_vmem();
     __syncthreads();
+    if (it + 1 < nst) {
+      if (it + 2 < nst) {
+        dma.issue(kb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, buf0);
+        dma.issue(vb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, buf0 + TILE);
+      }
+      st.stage(buf1, k0 + BN, klo, khi, R, wave, pq, g, p, qr, of, lane);
+      wait_vmem();
+      __syncthreads();
+    }
   }
+  f32x16 (&o)[NRB][D / 32] = st.o;
+  float (&m_run)[NRB] = st.m_run;
+  float (&l_run)[NRB] = st.l_run;
 
   // Partial of split e: normalised O_e (fp32) and LSE_e; empty -> O_e = 0, LSE_e = -inf.
   const int e = sigma * 4 + wave;
@@ -380,7 +432,7 @@ __global__ void mask_probe_kernel(const int32_t* cu_q, const int32_t* cu_k, int 
   if (idx >= (long)nq * nk) return;
   const int t = q0 + (int)(idx / nk), u = k0 + (int)(idx % nk);
   const int s = seq_of_token(cu_q, num_seqs, t);
-  const SeqGeom g = load_geom(cu_q, cu_k, s, mode);
+  const SeqGeom g = load_geom_lane(cu_q, cu_k, s, mode);
   const int pq = t - g.q_start;
   const int p0 = (pq / FWD_BM) * FWD_BM, p1 = min(p0 + FWD_BM, g.len_q);
   const int wp0 = p0 + ((pq - p0) / 32) * 32, wp1 = min(wp0 + 32, p1);
@@ -477,8 +529,9 @@ hipError_t launch_fwd_splitk(const FwdArgs& a, int nsb, int chunk, void* ws, hip
   if (a.dtype == 0)
     return a.d == 64 ? splitk_typed<__bf16, 64>(a, nsb, chunk, ws, st)
                      : splitk_typed<__bf16, 128>(a, nsb, chunk, ws, st);
-  return a.d == 64 ? splitk_typed<float, 64>(a, nsb, chunk, ws, st)
-                   : splitk_typed<float, 128>(a, nsb, chunk, ws, st);
+  // fp32 with head_dim 128: two 128-key stages do not fit in LDS; the planner never
+  // selects split-K for it.
+  return a.d == 64 ? splitk_typed<float, 64>(a, nsb, chunk, ws, st) : hipErrorNotSupported;
 }
 
 hipError_t launch_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int mode,

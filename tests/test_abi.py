@@ -62,6 +62,7 @@ def _fwd(lib, **kw):
     (dict(mode=3), BAD_MASK), (dict(mode=0, window=4), BAD_MASK),
     (dict(scale=float("inf")), BAD_SCALE), (dict(scale=float("nan")), BAD_SCALE),
     (dict(path=9), BAD_PLAN), (dict(path=2, max_q=4, hq=32, hkv=1), BAD_PLAN),
+    (dict(path=2, max_q=1, dtype=1, d=128), BAD_PLAN),
     (dict(q=None), NULL_PTR), (dict(lse=None), NULL_PTR), (dict(cu_k=None), NULL_PTR),
 ])
 def test_fwd_validation(lib, kw, code):
