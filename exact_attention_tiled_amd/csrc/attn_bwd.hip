@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   __shared__ float lse2s[BWD_BM];
   __shared__ float dvs[BWD_BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int hg = lane >> 5;
   const int w = xcd_logical_block(blockIdx.x, p.nlogical);
   if (w < 0) return;

@@ -168,9 +168,9 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nlogical) {
 // Swizzled LDS tiles filled by buffer -> LDS DMA.
 //
 // A tile row r of ROWB bytes occupies [r * ROWB, (r + 1) * ROWB) with its 16-byte chunk c
-// stored at slot c ^ (r & 7). The XOR spreads the same chunk of 8 consecutive rows over 8
-// different bank groups, so the column-wise MFMA operand reads are conflict-free without
-// padding (padding cannot be used: one DMA instruction writes 64 lanes x 16 bytes
+// stored at slot c ^ key(r), key a permutation of 0..7 (below). The XOR spreads the same
+// chunk of 8 consecutive rows over 8 different bank groups, so the MFMA operand reads avoid
+// bank conflicts without padding (padding cannot be used: one DMA instruction writes 64 lanes x 16 bytes
 // contiguously).
 //
 // buffer_load_dwordx4 ... lds writes lane l's 16 bytes to LDS at (wave-uniform base) +
@@ -179,7 +179,11 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nlogical) {
 // the sequence end (or the tensor end) are never read: the hardware range check returns
 // zeros for them.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ (row & 7); }
+// Row r's XOR key permutes 0..7 so that (i) 8 consecutive rows put one chunk in 8
+// different bank groups (row-wise ds_read_b128 of the K operand) and (ii) the 4 rows x 2
+// chunks read by 16 lanes of one ds_read_b64_tr_b16 land in 8 different bank groups.
+__device__ __forceinline__ int swz_key(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ swz_key(row); }
 
 template <int ROWB, int ROWS, int NWAVES>
 struct DmaStager {
@@ -289,17 +293,37 @@ struct Mma<__bf16, D> {
     }
   }
 
-  // o[db] += V_block^T P^T for the 32 keys of one block; p holds P^T in accumulator layout.
-  // K-slot t = 4 j + u of step s carries key 16 s + 8 j + 4 g + u, which is register
-  // 8 s + t of p, and is what the two transpose reads (rows +0 and +8) return.
-  __device__ static void pv(f32x16 (&o)[NDB], const f32x16& p, const char* vl, const Offsets& of,
-                            int lane) {
+  // P^T operand of the two 16-key steps of a 32-key block, rounded to bf16.
+  struct PPack {
     bf16x8 b[2];
+  };
+  // Rounds P to bf16 (round to nearest even, two values per instruction) and returns the
+  // fp32 sum of the unrounded values: the saved LSE keeps fp32 accuracy.
+  __device__ static float pack_p(const f32x16& p, PPack& pk) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    float sum = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      b[0][t] = (__bf16)p[t];
-      b[1][t] = (__bf16)p[8 + t];
+    for (int h = 0; h < 2; ++h) {
+      i32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 x = {p[8 * h + 2 * i], p[8 * h + 2 * i + 1]};
+        w[i] = __builtin_bit_cast(int, __builtin_convertvector(x, bf16x2));
+        sum += x[0] + x[1];
+      }
+      pk.b[h] = __builtin_bit_cast(bf16x8, w);
     }
+    return sum;
+  }
+
+  // o[db] += V_block^T P^T for the 32 keys of one block.
+  // K-slot t = 4 j + u of step s carries key 16 s + 8 j + 4 g + u, which is register
+  // 8 s + t of the accumulator-layout P, and is what the two transpose reads (rows +0 and
+  // +8) return.
+  __device__ static void pv(f32x16 (&o)[NDB], const PPack& pk, const char* vl, const Offsets& of,
+                            int lane) {
+    const bf16x8(&b)[2] = pk.b;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -356,9 +380,21 @@ struct Mma<float, D> {
     }
   }
 
+  struct PPack {
+    f32x16 p;
+  };
+  __device__ static float pack_p(const f32x16& p, PPack& pk) {
+    pk.p = p;
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += p[r];
+    return sum;
+  }
+
   // Step r contracts the two keys held in register r by the two lane halves.
-  __device__ static void pv(f32x16 (&o)[NDB], const f32x16& p, const char* vl, const Offsets&,
+  __device__ static void pv(f32x16 (&o)[NDB], const PPack& pk, const char* vl, const Offsets&,
                             int lane) {
+    const f32x16& p = pk.p;
     const int i = lane & 31, g = lane >> 5;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

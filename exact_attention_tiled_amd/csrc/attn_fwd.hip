@@ -33,14 +33,22 @@ struct FwdParams {
   int blocks_per_kvh, chunk, nsplit;
 };
 
+// The exponent offset of a row moves only when a tile's maximum exceeds it by more than
+// this many powers of two (or the row has seen nothing yet). Any offset gives the same
+// O = acc / l and LSE = offset + log2 l; bounding every P by 2^8 keeps all terms finite, and
+// most tiles then skip the accumulator rescale.
+constexpr float RESCALE_THRESHOLD = 8.0f;
+
 // One online-softmax step for NK key blocks of 32 keys held in accumulator layout.
 // s[kb][r] is the raw (sign-folded) dot product of this lane's query with key
-// kpos0 + 32 kb + key_of_reg(r, g); on return it holds P (fp32, not yet normalised).
-template <int NK, int D>
-__device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], bool need_mask, int pq, int kpos0,
-                                             const SeqGeom& g, int mode, int window, float c2,
-                                             float& m_run, float& l_run, f32x16 (&o)[D / 32],
-                                             int lane) {
+// kpos0 + 32 kb + key_of_reg(r, g); pk receives P (not yet normalised) as the PV operand.
+// m_run is in log2 units of the scaled logits; l_run is this lane's partial denominator
+// (the other half of the row lives in lane l ^ 32).
+template <typename M, int NK, int D>
+__device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack (&pk)[NK],
+                                             bool need_mask, int pq, int kpos0, const SeqGeom& g,
+                                             int mode, int window, float c2, float& m_run,
+                                             float& l_run, f32x16 (&o)[D / 32], int lane) {
   const int hg = lane >> 5;
   if (need_mask) {
 #pragma unroll
@@ -58,27 +66,34 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], bool need_mask, in
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
   mx = fmaxf(mx, swap_halves(mx));
   const float mt = (mx == neg_inf()) ? neg_inf() : mx * c2;
-  const float m_new = fmaxf(m_run, mt);
-  const float base = (m_new == neg_inf()) ? 0.0f : m_new;
-  const float alpha = fast_exp2(m_run - base);  // 0 while the row has seen nothing
-  float rs = 0.0f;
-#pragma unroll
-  for (int kb = 0; kb < NK; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = s[kb][r];
-      const float e0 = fast_exp2(fmaf(x, c2, -base));
-      const float e = (need_mask & (x == neg_inf())) ? 0.0f : e0;
-      s[kb][r] = e;
-      rs += e;
-    }
-  l_run = l_run * alpha + rs;
-  m_run = m_new;
-  // Skip the accumulator rescale when no row of the wave moved its maximum.
-  if (__any(alpha != 1.0f)) {
+  const bool grow = mt > m_run + RESCALE_THRESHOLD;
+  if (__any(grow)) {
+    const float m_new = grow ? mt : m_run;
+    const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // 0 if nothing seen yet
+    l_run *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    m_run = m_new;
   }
+  const float base = (m_run == neg_inf()) ? 0.0f : m_run;
+  if (need_mask) {
+    // Excluded entries hold -inf; force their weight to exactly 0 (also when c2 == 0).
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = s[kb][r];
+        const float e0 = fast_exp2(fmaf(x, c2, -base));
+        s[kb][r] = (x == neg_inf()) ? 0.0f : e0;
+      }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(fmaf(s[kb][r], c2, -base));
+  }
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) l_run += M::pack_p(s[kb], pk[kb]);
 }
 
 // Running state of one prefill wave (32 query rows) and its step over one 64-key stage.
@@ -110,9 +125,11 @@ struct PrefillWave {
       sacc[kb] = f32x16{};
       M::qk(sacc[kb], buf + kb * 32 * ROWB, qr, of, lane);
     }
-    softmax_step<2, D>(sacc, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run, l_run, o, lane);
+    typename M::PPack pk[2];
+    softmax_step<M, 2, D>(sacc, pk, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run, l_run, o,
+                          lane);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) M::pv(o, sacc[kb], buf + TILE + kb * 32 * ROWB, of, lane);
+    for (int kb = 0; kb < 2; ++kb) M::pv(o, pk[kb], buf + TILE + kb * 32 * ROWB, of, lane);
   }
 };
 
@@ -130,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];  // K tile, then V tile
   __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int w = xcd_logical_block(blockIdx.x, p.nlogical);
   if (w < 0) return;
   const int h = w / p.nslots, slot = w - h * p.nslots;
@@ -263,9 +280,10 @@ struct SplitkWave {
           sacc[0][r] = ((kk >= cw0) & (kk < cw1)) ? sacc[0][r] : neg_inf();
         }
       }
-      softmax_step<1, D>(sacc, cls == 1 || clip, pq[rb], kw, g, p.mode, p.window, p.c2,
-                         m_run[rb], l_run[rb], o[rb], lane);
-      M::pv(o[rb], sacc[0], buf + TILE + 32 * wave * ROWB, of, lane);
+      typename M::PPack pk[1];
+      softmax_step<M, 1, D>(sacc, pk, cls == 1 || clip, pq[rb], kw, g, p.mode, p.window, p.c2,
+                            m_run[rb], l_run[rb], o[rb], lane);
+      M::pv(o[rb], pk[0], buf + TILE + 32 * wave * ROWB, of, lane);
     }
   }
 };
@@ -286,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int b = blockIdx.x;
   const int sigma = b % p.blocks_per_kvh;
   const int kvh = (b / p.blocks_per_kvh) % p.hkv;
