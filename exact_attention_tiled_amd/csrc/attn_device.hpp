@@ -47,6 +47,17 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32);
 }
 
+// max / sum of x over lanes l and l ^ 32, in VALU only: v_permlane32_swap(x, x) yields the
+// low half and the high half of x, each replicated to both halves of the wave.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------------------
 // Mask unit. Sequence geometry comes from cu_seqlens; positions are always in-sequence
 // (0-based), never packed offsets. `off` is the alignment shift of the causal diagonal:
@@ -168,9 +179,8 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nlogical) {
 // Swizzled LDS tiles filled by buffer -> LDS DMA.
 //
 // A tile row r of ROWB bytes occupies [r * ROWB, (r + 1) * ROWB) with its 16-byte chunk c
-// stored at slot c ^ key(r), key a permutation of 0..7 (below). The XOR spreads the same
-// chunk of 8 consecutive rows over 8 different bank groups, so the MFMA operand reads avoid
-// bank conflicts without padding (padding cannot be used: one DMA instruction writes 64 lanes x 16 bytes
+// stored at slot c ^ key(r) (key below). The XOR spreads the chunks the MFMA operand reads
+// touch together over different bank groups, so they avoid bank conflicts without padding (padding cannot be used: one DMA instruction writes 64 lanes x 16 bytes
 // contiguously).
 //
 // buffer_load_dwordx4 ... lds writes lane l's 16 bytes to LDS at (wave-uniform base) +
@@ -179,11 +189,19 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nlogical) {
 // the sequence end (or the tensor end) are never read: the hardware range check returns
 // zeros for them.
 // ---------------------------------------------------------------------------------------
-// Row r's XOR key permutes 0..7 so that (i) 8 consecutive rows put one chunk in 8
-// different bank groups (row-wise ds_read_b128 of the K operand) and (ii) the 4 rows x 2
-// chunks read by 16 lanes of one ds_read_b64_tr_b16 land in 8 different bank groups.
-__device__ __forceinline__ int swz_key(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ swz_key(row); }
+// gfx950 LDS serves 256 bytes per cycle (64 banks; measured with the bank-conflict
+// counter). Row r's XOR key must therefore (i) give 16 consecutive rows 16 different
+// 16-byte slots for one chunk (row-wise ds_read_b128 of the K operand, 16 lanes per cycle)
+// and (ii) put the 4 rows read by half a wave of ds_read_b64_tr_b16 (4 chunks each) in 4
+// different groups of 4 slots. For 256-byte rows the key is the 4x4 bit transpose of
+// r mod 16; for 128-byte rows (two rows per 256-byte bank cycle) a 3-bit key of r / 2.
+template <int ROWB>
+__device__ __forceinline__ int swz_key(int row) {
+  if (ROWB >= 256) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+template <int ROWB>
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ swz_key<ROWB>(row); }
 
 template <int ROWB, int ROWS, int NWAVES>
 struct DmaStager {
@@ -200,7 +218,7 @@ struct DmaStager {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int row = first_row + i * RPI + lane / C;
-      voff[i] = (uint32_t)row * row_stride + (uint32_t)(swz_chunk(row, lane % C) << 4);
+      voff[i] = (uint32_t)row * row_stride + (uint32_t)(swz_chunk<ROWB>(row, lane % C) << 4);
     }
   }
   // Rows [0, valid_rows) of the tile start at `rows` (global) with stride `row_stride`.
@@ -251,20 +269,22 @@ struct Mma<__bf16, D> {
 
   // Per-lane LDS byte offsets, fixed for the whole kernel.
   struct Offsets {
-    int k[QREGS];   // K operand of step s: row l % 32, chunk 2 s + l / 32
-    int v[NDB];     // V^T operand of head-dim block db (row part 4 g + (l % 16) / 4)
+    int k[QREGS];    // K operand of step s: row l % 32, chunk 2 s + l / 32
+    int v[NDB][2];   // V^T operand of head-dim block db, rows 8 j + 4 g + (l % 16) / 4
   };
   __device__ static Offsets offsets(int lane) {
     Offsets o;
     const int i = lane & 31, g = lane >> 5;
 #pragma unroll
-    for (int s = 0; s < QREGS; ++s) o.k[s] = i * ROWB + (swz_chunk(i, 2 * s + g) << 4);
+    for (int s = 0; s < QREGS; ++s) o.k[s] = i * ROWB + (swz_chunk<ROWB>(i, 2 * s + g) << 4);
     const int a16 = lane & 15, hh = (lane >> 4) & 1;
     const int x = 4 * g + (a16 >> 2);  // row within an aligned group of 8
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int c = 4 * db + 2 * hh + ((a16 & 3) >> 1);
-      o.v[db] = x * ROWB + (swz_chunk(x, c) << 4) + 8 * (a16 & 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        o.v[db][j] = x * ROWB + (swz_chunk<ROWB>(8 * j + x, c) << 4) + 8 * (a16 & 1);
     }
     return o;
   }
@@ -296,6 +316,15 @@ struct Mma<__bf16, D> {
   // P^T operand of the two 16-key steps of a 32-key block, rounded to bf16.
   struct PPack {
     bf16x8 b[2];
+    // Registers 2i, 2i+1 of the accumulator-layout P (round to nearest even).
+    __device__ __forceinline__ void set_pair(int i, float e0, float e1) {
+      typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+      typedef __attribute__((ext_vector_type(2))) float f32x2;
+      const f32x2 x = {e0, e1};
+      i32x4 w = __builtin_bit_cast(i32x4, b[i >> 2]);
+      w[i & 3] = __builtin_bit_cast(int, __builtin_convertvector(x, bf16x2));
+      b[i >> 2] = __builtin_bit_cast(bf16x8, w);
+    }
   };
   // Rounds P to bf16 (round to nearest even, two values per instruction) and returns the
   // fp32 sum of the unrounded values: the saved LSE keeps fp32 accuracy.
@@ -328,9 +357,10 @@ struct Mma<__bf16, D> {
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const char* p0 = vl + 16 * s * ROWB + of.v[db];
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * ROWB));
+        const char* p0 = vl + 16 * s * ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + of.v[db][0]));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * ROWB + of.v[db][1]));
         const i32x4 cat = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
                            __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), b[s],
@@ -368,7 +398,9 @@ struct Mma<float, D> {
   }
 
   // Element e of row r lives at r * ROWB + (swz(r, e / 4) << 4) + 4 (e % 4).
-  __device__ static int at(int row, int e) { return row * ROWB + (swz_chunk(row, e >> 2) << 4) + 4 * (e & 3); }
+  __device__ static int at(int row, int e) {
+    return row * ROWB + (swz_chunk<ROWB>(row, e >> 2) << 4) + 4 * (e & 3);
+  }
 
   __device__ static void qk(f32x16& acc, const char* kl, const QOperand (&qr)[QREGS], const Offsets&,
                             int lane) {
@@ -382,6 +414,10 @@ struct Mma<float, D> {
 
   struct PPack {
     f32x16 p;
+    __device__ __forceinline__ void set_pair(int i, float e0, float e1) {
+      p[2 * i] = e0;
+      p[2 * i + 1] = e1;
+    }
   };
   __device__ static float pack_p(const f32x16& p, PPack& pk) {
     pk.p = p;

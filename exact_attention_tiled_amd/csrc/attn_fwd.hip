@@ -64,7 +64,7 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack 
   for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = max_halves(mx);
   const float mt = (mx == neg_inf()) ? neg_inf() : mx * c2;
   const bool grow = mt > m_run + RESCALE_THRESHOLD;
   if (__any(grow)) {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   const float m_run = st.m_run, l_run = st.l_run;
 
   // Epilogue: O = acc / l (exactly +0.0 for rows that saw no allowed key), natural-log LSE.
-  const float lt = l_run + swap_halves(l_run);
+  const float lt = sum_halves(l_run);
   const bool nonempty = lt > 0.0f;
   const float inv = nonempty ? 1.0f / lt : 0.0f;
   if (qvalid) {
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
   const int hg = lane >> 5;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const float lt = l_run[rb] + swap_halves(l_run[rb]);
+    const float lt = sum_halves(l_run[rb]);
     const bool nonempty = lt > 0.0f;
     const float inv = nonempty ? 1.0f / lt : 0.0f;
     if (!rvalid[rb]) continue;
