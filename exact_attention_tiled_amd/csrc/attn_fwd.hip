@@ -120,16 +120,22 @@ struct PrefillWave {
     const int cls = block_class(wp0, wp1, k0, k0 + FWD_BN, g, p.mode, p.window);
     if (cls == 0) return;
     f32x16 sacc[2];
+    // The two waves sharing a SIMD alternate between MFMA and softmax phases: a wave
+    // entering a contraction takes issue priority so the other wave's VALU work overlaps.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x16{};
       M::qk(sacc[kb], buf + kb * 32 * ROWB, qr, of, lane);
     }
+    __builtin_amdgcn_s_setprio(0);
     typename M::PPack pk[2];
     softmax_step<M, 2, D>(sacc, pk, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run, l_run, o,
                           lane);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) M::pv(o, pk[kb], buf + TILE + kb * 32 * ROWB, of, lane);
+    __builtin_amdgcn_s_setprio(0);
   }
 };
 
