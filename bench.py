@@ -37,10 +37,14 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["exact_attention_tiled_amd/csrc/attn_device.hpp",
-                  "exact_attention_tiled_amd/csrc/attn_fwd.hip",
-                  "exact_attention_tiled_amd/csrc/attn_bwd.hip",
-                  "exact_attention_tiled_amd/csrc/attn_internal.h"]
+_CSRC = "exact_attention_tiled_amd/csrc/"
+# Sources that determine each kernel's machine code (a stored counter reading is only
+# reported while these are unchanged).
+KERNEL_SOURCES = {
+    "fwd_prefill_kernel": [_CSRC + "attn_device.hpp", _CSRC + "attn_fwd.hip", _CSRC + "attn_internal.h"],
+    "fwd_splitk_kernel": [_CSRC + "attn_device.hpp", _CSRC + "attn_fwd.hip", _CSRC + "attn_internal.h"],
+    "bwd_main_kernel": [_CSRC + "attn_device.hpp", _CSRC + "attn_bwd.hip", _CSRC + "attn_internal.h"],
+}
 
 
 # ----------------------------------------------------------------------------------------
@@ -79,9 +83,9 @@ def bwd_bytes(w) -> int:
     return el * (w.q.size * 4 + w.k.size * 2 + w.v.size * 2) + 4 * w.hq * w.total_q
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "fwd_prefill_kernel") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -96,7 +100,7 @@ def stored_traffic(kernel: str, workload: str):
     with open(path) as f:
         data = json.load(f)
     ent = data.get("entries", {}).get(f"{kernel}@{workload}")
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -385,7 +389,8 @@ def main():
         line["secondary"] = sec
     line["env"] = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
                    "hip": getattr(torch.version, "hip", None), "host": platform.node(),
-                   "library_version": eat.attn_version(), "kernel_source_hash": kernel_source_hash()}
+                   "library_version": eat.attn_version(),
+                   "kernel_source_hash": kernel_source_hash(kernel)}
     print(json.dumps(line))
 
 
