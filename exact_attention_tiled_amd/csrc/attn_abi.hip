@@ -278,8 +278,11 @@ int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32
     FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, num_seqs, total_q, total_k,
                           max_q, max_k, hq, hkv, d, dtype, 1.0f, mode, window, nullptr, nullptr);
     std::snprintf(buf, len,
-                  "path=prefill dtype=%s d=%d tile=%dx%d waves=4 grid=%d workspace=0 version=%d",
-                  dt, d, attn::FWD_BM, attn::FWD_BN, attn::fwd_prefill_grid(a), ATTN_VERSION);
+                  "path=prefill dtype=%s d=%d tile=%dx%d waves=4 order=%s grid=%d workspace=0 "
+                  "version=%d",
+                  dt, d, attn::FWD_BM, attn::FWD_BN,
+                  attn::equal_lengths(a) ? "largest_first" : "slots", attn::fwd_prefill_grid(a),
+                  ATTN_VERSION);
   } else {
     std::snprintf(buf, len,
                   "path=splitk dtype=%s d=%d stage=%d rows_per_kvhead<=%d blocks_per_kvhead=%d "

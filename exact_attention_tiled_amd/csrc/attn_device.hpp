@@ -245,6 +245,76 @@ struct DmaStager {
   }
 };
 
+// ---------------------------------------------------------------------------------------
+// V^T tiles for the bf16 PV contraction.
+//
+// The PV MFMA needs, per lane, 8 keys of one head-dim index: a column of the row-major V
+// tile. Reading columns with the transposing LDS read moves only ~70 B/clk per CU on gfx950
+// (measured), against ~220 B/clk for row-wise ds_read_b128, and every wave of a workgroup
+// would repeat it. Instead the tile is transposed once per stage on its way into LDS:
+// thread t loads 4 consecutive keys x 8 head-dim values (four 16-byte buffer loads, zeros
+// past the sequence end), transposes that 4 x 8 block in registers with byte permutes, and
+// writes eight 8-byte rows of V^T. The PV operands are then plain 16-byte reads.
+//
+// Layout: row d (head-dim index) holds the BN keys of the stage at a pitch of 2 BN + 16
+// bytes (the 16-byte pad makes both the writes and the operand reads conflict-free on the
+// 64-bank LDS). Within each group of 16 keys, key 8 j + 4 h + u sits at position
+// 8 h + 4 j + u (bits 2 and 3 of the key index swapped), the order in which the P operand
+// carries keys, so each lane's 8 keys of one MFMA step are contiguous.
+// ---------------------------------------------------------------------------------------
+template <int D, int BN>
+struct VtStager {
+  static constexpr int PITCH = 2 * BN + 16;
+  static constexpr int TILE_BYTES = D * PITCH;
+  static constexpr int GROUPS = BN / 4;                   // 4-key groups per stage
+  static constexpr int ITEMS = GROUPS * (D / 8);          // (key group, head-dim chunk)
+  static_assert(BN == 64 && ITEMS <= 256, "one item per thread of a 256-thread workgroup");
+  uint32_t voff;   // global byte offset of key 4 m, chunk c, within the stage's rows
+  int woff;        // LDS byte offset of row 8 c, position 4 m'
+  bool active;
+  i32x4 r[4];
+
+  __device__ __forceinline__ void init(int tid, uint32_t row_stride) {
+    const int m = tid % GROUPS, c = tid / GROUPS;
+    active = tid < ITEMS;
+    voff = (uint32_t)(4 * m) * row_stride + (uint32_t)(c * 16);
+    const int mp = (m & ~3) | ((m & 1) << 1) | ((m >> 1) & 1);
+    woff = 8 * c * PITCH + 8 * mp;
+  }
+  // Rows [0, valid_rows) of the stage start at `rows` (global) with stride `row_stride`.
+  __device__ __forceinline__ void issue(const char* rows, int valid_rows, uint32_t row_stride) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int v = valid_rows < 0 ? 0 : (valid_rows > BN ? BN : valid_rows);
+    const uint64_t base = (uint64_t)rows;
+    const uint64_t ubase = ((uint64_t)(uint32_t)uniform((int)(base >> 32)) << 32) |
+                           (uint32_t)uniform((int)(uint32_t)base);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(ubase), (short)0, uniform((int)((uint32_t)v * row_stride)),
+        0x00020000);
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        r[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rsrc, (int)(voff + (uint32_t)u * row_stride), 0, 0));
+    }
+#endif
+  }
+  // Transpose the four loaded keys into eight V^T rows of 4 keys (8 bytes) each.
+  __device__ __forceinline__ void write(char* lds_tile) const {
+    if (!active) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // head-dim 2e: low halves; 2e + 1: high halves (bytes 0,1 / 2,3 of each dword)
+      const int lo01 = (int)__builtin_amdgcn_perm((uint32_t)r[1][e], (uint32_t)r[0][e], 0x05040100u);
+      const int lo23 = (int)__builtin_amdgcn_perm((uint32_t)r[3][e], (uint32_t)r[2][e], 0x05040100u);
+      const int hi01 = (int)__builtin_amdgcn_perm((uint32_t)r[1][e], (uint32_t)r[0][e], 0x07060302u);
+      const int hi23 = (int)__builtin_amdgcn_perm((uint32_t)r[3][e], (uint32_t)r[2][e], 0x07060302u);
+      *reinterpret_cast<i32x2*>(lds_tile + woff + (2 * e) * PITCH) = i32x2{lo01, lo23};
+      *reinterpret_cast<i32x2*>(lds_tile + woff + (2 * e + 1) * PITCH) = i32x2{hi01, hi23};
+    }
+  }
+};
+
 // Wait for this thread's outstanding DMA / global loads (before the barrier that
 // publishes an LDS stage).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -271,6 +341,7 @@ struct Mma<__bf16, D> {
   struct Offsets {
     int k[QREGS];    // K operand of step s: row l % 32, chunk 2 s + l / 32
     int v[NDB][2];   // V^T operand of head-dim block db, rows 8 j + 4 g + (l % 16) / 4
+    int vt[NDB];     // V^T tile operand of head-dim block db: row 32 db + l % 32, +16 (l / 32)
   };
   __device__ static Offsets offsets(int lane) {
     Offsets o;
@@ -286,6 +357,9 @@ struct Mma<__bf16, D> {
       for (int j = 0; j < 2; ++j)
         o.v[db][j] = x * ROWB + (swz_chunk<ROWB>(8 * j + x, c) << 4) + 8 * (a16 & 1);
     }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      o.vt[db] = (32 * db + i) * VtStager<D, 64>::PITCH + 16 * g;
     return o;
   }
 
@@ -365,6 +439,78 @@ struct Mma<__bf16, D> {
                            __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), b[s],
                                                         o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // Operand reads are issued PF MFMAs ahead of their use (one MFMA is shorter than an LDS
+  // read's latency), and consecutive MFMAs write different accumulators. The scheduling
+  // groups keep the compiler from clustering the reads back next to their MFMAs.
+  static constexpr int PF = 4;
+
+  // acc[kb] += K_kb Q^T for both 32-key blocks of a 64-key stage at `kt`.
+  __device__ static void qk2(f32x16 (&acc)[2], const char* kt, const QOperand (&qr)[QREGS],
+                             const Offsets& of) {
+    constexpr int N = 2 * QREGS;  // MFMA i: block i & 1, head-dim step i >> 1
+    bf16x8 a[N];
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(kt + (i & 1) * 32 * ROWB + of.k[i >> 1]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + PF < N) {
+        const int j = i + PF;
+        a[j] = *reinterpret_cast<const bf16x8*>(kt + (j & 1) * 32 * ROWB + of.k[j >> 1]);
+      }
+      acc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qr[i >> 1], acc[i & 1], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int i = 0; i < N - PF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  }
+
+  // o[db] += V^T P^T over both 32-key blocks of a V^T tile (VtStager layout); MFMA i takes
+  // block i / (2 NDB), step (i / NDB) & 1, head-dim block i % NDB.
+  __device__ static void pv2(f32x16 (&o)[NDB], const PPack (&pk)[2], const char* vt_tile,
+                             const Offsets& of) {
+    constexpr int N = 4 * NDB;
+    bf16x8 a[N];
+#define ATTN_VT_OPERAND(i) \
+  (*reinterpret_cast<const bf16x8*>(vt_tile + of.vt[(i) % NDB] + 64 * ((i) / (2 * NDB)) + 32 * (((i) / NDB) & 1)))
+#pragma unroll
+    for (int i = 0; i < PF; ++i) a[i] = ATTN_VT_OPERAND(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + PF < N) a[i + PF] = ATTN_VT_OPERAND(i + PF);
+      o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a[i], pk[i / (2 * NDB)].b[(i / NDB) & 1], o[i % NDB], 0, 0, 0);
+    }
+#undef ATTN_VT_OPERAND
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int i = 0; i < N - PF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  }
+
+  // o[db] += V_block^T P^T for the 32 keys of block kb of a V^T tile (VtStager layout):
+  // step s reads positions 32 kb + 16 s + 8 (l / 32) + 0..7 of row 32 db + l % 32, which
+  // hold keys 32 kb + 16 s + 8 j + 4 (l / 32) + u for slot t = 4 j + u: the keys the P
+  // operand carries in slot t.
+  __device__ static void pv_t(f32x16 (&o)[NDB], const PPack& pk, const char* vt_tile, int kb,
+                              const Offsets& of) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt_tile + of.vt[db] + 64 * kb + 32 * s);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk.b[s], o[db], 0, 0, 0);
       }
     }
   }

@@ -8,6 +8,9 @@
 // and divide by the denominator at the end ("Efficient Attention: Formal Correctness",
 // "The FlashAttention Proof": online softmax recurrence; "Causal Mask and Ragged Sequence
 // Layouts", sections 1-4: in-sequence positions, out-of-range lanes, alignment, zero rows).
+#include <algorithm>
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "attn_internal.h"
 
@@ -25,8 +28,10 @@ struct FwdParams {
   int mode, window;
   void* out;
   float* lse;
-  // prefill
+  // prefill: slot order (any lengths) or, for batches whose sequences all have the same
+  // lengths, tiles of `uni_ntiles` per sequence enumerated heaviest first (uni_ntiles > 0)
   int nslots, nlogical;
+  int uni_ntiles, npairs;
   // split-K
   float* part_o;
   float* part_lse;
@@ -96,6 +101,39 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack 
   for (int kb = 0; kb < NK; ++kb) l_run += M::pack_p(s[kb], pk[kb]);
 }
 
+// The (query head, sequence, query tile) of this workgroup; false for padding blocks.
+template <int BM>
+__device__ __forceinline__ bool prefill_tile(const FwdParams& p, int& h, int& s, int& tile,
+                                             SeqGeom& g) {
+  if (p.uni_ntiles > 0) {
+    // Equal-length batch. Block b takes tile rank b / npairs of (sequence, head) pair
+    // b % npairs, so every tile of a given cost is dispatched before any cheaper one
+    // (largest-first list scheduling), on every XCD alike. Heads are enumerated K/V head
+    // fastest: with npairs a multiple of 8, the round-robin XCD assignment b % 8 then keeps
+    // every query head of one GQA group, and all tiles of one (sequence, K/V head), on
+    // the same XCD and its L2.
+    const int b = blockIdx.x;
+    const int rank = b / p.npairs, pair = b - rank * p.npairs;
+    s = pair / p.hq;
+    const int hp = pair - s * p.hq;
+    h = (hp % p.hkv) * p.group + hp / p.hkv;
+    g = load_geom(p.cu_q, p.cu_k, s, p.mode);
+    const int ntiles = (g.len_q + BM - 1) / BM;
+    tile = p.uni_ntiles - 1 - rank;  // latest (heaviest under causal masks) tiles first
+    return tile < ntiles;
+  }
+  const int w = xcd_logical_block(blockIdx.x, p.nlogical);
+  if (w < 0) return false;
+  h = w / p.nslots;
+  const int slot = w - h * p.nslots;
+  s = seq_of_slot<BM>(p.cu_q, p.num_seqs, slot);
+  g = load_geom(p.cu_q, p.cu_k, s, p.mode);
+  const int ntiles = (g.len_q + BM - 1) / BM;
+  const int j = slot - (g.q_start / BM + s);
+  tile = ntiles - 1 - j;  // latest (heaviest under causal masks) tiles first
+  return j < ntiles;
+}
+
 // Running state of one prefill wave (32 query rows) and its step over one 64-key stage.
 template <typename T, int D>
 struct PrefillWave {
@@ -110,33 +148,72 @@ struct PrefillWave {
     l_run = 0.0f;
   }
 
-  // One stage of FWD_BN keys starting at key position k0, staged at `buf` (K tile, then
-  // V tile). The wave's rows are query positions [wp0, wp1); this lane's query is pq.
-  __device__ __forceinline__ void stage(const char* buf, int k0, int wp0, int wp1, int pq,
-                                        const SeqGeom& g, const FwdParams& p,
+  // One stage of FWD_BN keys starting at key position k0: K tile at `kt` (row-major), V at
+  // `vt` (V^T tile for bf16, row-major for fp32). The wave's rows are query positions
+  // [wp0, wp1); this lane's query is pq.
+  __device__ __forceinline__ void stage(const char* kt, const char* vt, int k0, int wp0, int wp1,
+                                        int pq, const SeqGeom& g, const FwdParams& p,
                                         const typename M::QOperand (&qr)[M::QREGS],
                                         const typename M::Offsets& of, int lane) {
-    constexpr int ROWB = M::ROWB, TILE = FWD_BN * ROWB;
+    constexpr int ROWB = M::ROWB;
     const int cls = block_class(wp0, wp1, k0, k0 + FWD_BN, g, p.mode, p.window);
     if (cls == 0) return;
     f32x16 sacc[2];
     // The two waves sharing a SIMD alternate between MFMA and softmax phases: a wave
     // entering a contraction takes issue priority so the other wave's VALU work overlaps.
     __builtin_amdgcn_s_setprio(1);
+    if constexpr (std::is_same<T, __bf16>::value) {
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+      M::qk2(sacc, kt, qr, of);
+    } else {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      M::qk(sacc[kb], buf + kb * 32 * ROWB, qr, of, lane);
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+        M::qk(sacc[kb], kt + kb * 32 * ROWB, qr, of, lane);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
     typename M::PPack pk[2];
     softmax_step<M, 2, D>(sacc, pk, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run, l_run, o,
                           lane);
     __builtin_amdgcn_s_setprio(1);
+    if constexpr (std::is_same<T, __bf16>::value) {
+      M::pv2(o, pk, vt, of);
+    } else {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) M::pv(o, pk[kb], buf + TILE + kb * 32 * ROWB, of, lane);
+      for (int kb = 0; kb < 2; ++kb) M::pv(o, pk[kb], vt + kb * 32 * ROWB, of, lane);
+    }
     __builtin_amdgcn_s_setprio(0);
   }
+};
+
+// V staging of the prefill: bf16 transposes V into V^T tiles through registers (the
+// loads of stage j+1 are in flight while stage j is computed, and written to LDS after
+// it); fp32 copies row-major V tiles by DMA like K.
+template <typename T, int D>
+struct PrefillVStage {
+  DmaStager<Mma<T, D>::ROWB, FWD_BN, 4> dma;
+  static constexpr int TILE_BYTES = FWD_BN * Mma<T, D>::ROWB;
+  __device__ __forceinline__ void init(int wave, int lane, int, uint32_t rstride) {
+    dma.init(wave, lane, rstride);
+  }
+  __device__ __forceinline__ void issue(const char* rows, int valid, uint32_t rstride, char* tile) {
+    dma.issue(rows, valid, rstride, tile);
+  }
+  __device__ __forceinline__ void commit(char*) const {}
+};
+template <int D>
+struct PrefillVStage<__bf16, D> {
+  VtStager<D, FWD_BN> vt;
+  static constexpr int TILE_BYTES = VtStager<D, FWD_BN>::TILE_BYTES;
+  __device__ __forceinline__ void init(int, int, int tid, uint32_t rstride) {
+    vt.init(tid, rstride);
+  }
+  __device__ __forceinline__ void issue(const char* rows, int valid, uint32_t rstride, char*) {
+    vt.issue(rows, valid, rstride);
+  }
+  __device__ __forceinline__ void commit(char* tile) const { vt.write(tile); }
 };
 
 // ---------------------------------------------------------------------------------------
@@ -148,21 +225,17 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   typedef Mma<T, D> M;
   constexpr int BM = FWD_BM, BN = FWD_BN, ROWB = M::ROWB;
-  constexpr int TILE = BN * ROWB;
-  static_assert(2 * 2 * TILE <= LDS_BYTES, "two K/V stages must fit in LDS");
-  __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];  // K tile, then V tile
-  __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];
+  constexpr int KTILE = BN * ROWB, VTILE = PrefillVStage<T, D>::TILE_BYTES;
+  static_assert(2 * (KTILE + VTILE) <= LDS_BYTES, "two K/V stages must fit in LDS");
+  __shared__ __attribute__((aligned(1024))) char kbuf0[KTILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[KTILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[VTILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[VTILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-  const int w = xcd_logical_block(blockIdx.x, p.nlogical);
-  if (w < 0) return;
-  const int h = w / p.nslots, slot = w - h * p.nslots;
-  const int s = seq_of_slot<BM>(p.cu_q, p.num_seqs, slot);
-  const SeqGeom g = load_geom(p.cu_q, p.cu_k, s, p.mode);
-  const int ntiles = (g.len_q + BM - 1) / BM;
-  const int j = slot - (g.q_start / BM + s);
-  if (j >= ntiles) return;
-  const int tile = ntiles - 1 - j;  // latest (heaviest under causal masks) tiles first
+  int h, s, tile;
+  SeqGeom g;
+  if (!prefill_tile<BM>(p, h, s, tile, g)) return;
   const int p0 = tile * BM, p1 = min(p0 + BM, g.len_q);
   const int kvh = h / p.group;
 
@@ -185,32 +258,40 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   const char* vb0 = static_cast<const char*>(p.v) + ((size_t)g.k_start * p.hkv + kvh) * D * sizeof(T);
   DmaStager<ROWB, BN, 4> dma;
   dma.init(wave, lane, rstride);
+  PrefillVStage<T, D> vst;
+  vst.init(wave, lane, tid, rstride);
 
   PrefillWave<T, D> st;
   st.init();
 
+  // Stage j lives in buffer j % 2. The loads of stage j+1 are issued before stage j is
+  // computed; the barrier after stage j publishes stage j+1 (the V^T transpose-write happens
+  // once its loads have landed) and frees buffer j % 2 for stage j+2.
   if (nst > 0) {
-    dma.issue(kb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, buf0);
-    dma.issue(vb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, buf0 + TILE);
+    dma.issue(kb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, kbuf0);
+    vst.issue(vb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, vbuf0);
   }
   wait_vmem();
+  if (nst > 0) vst.commit(vbuf0);
   __syncthreads();
   for (int it = 0; it < nst; it += 2) {
     const int k0 = kstart + it * BN;
     if (it + 1 < nst) {
-      dma.issue(kb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, buf1);
-      dma.issue(vb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, buf1 + TILE);
+      dma.issue(kb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, kbuf1);
+      vst.issue(vb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, vbuf1);
     }
-    st.stage(buf0, k0, wp0, wp1, pq, g, p, qr, of, lane);
+    st.stage(kbuf0, vbuf0, k0, wp0, wp1, pq, g, p, qr, of, lane);
     wait_vmem();
+    if (it + 1 < nst) vst.commit(vbuf1);
     __syncthreads();
     if (it + 1 < nst) {
       if (it + 2 < nst) {
-        dma.issue(kb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, buf0);
-        dma.issue(vb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, buf0 + TILE);
+        dma.issue(kb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, kbuf0);
+        vst.issue(vb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, vbuf0);
       }
-      st.stage(buf1, k0 + BN, wp0, wp1, pq, g, p, qr, of, lane);
+      st.stage(kbuf1, vbuf1, k0 + BN, wp0, wp1, pq, g, p, qr, of, lane);
       wait_vmem();
+      if (it + 2 < nst) vst.commit(vbuf0);
       __syncthreads();
     }
   }
@@ -236,6 +317,264 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
     if (hg == 0)
       p.lse[(size_t)h * p.total_q + g.q_start + pq] =
           nonempty ? (m_run + fast_log2(lt)) * LN2 : neg_inf();
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16 prefill, software-pipelined within each wave. Iteration j issues the MFMAs of
+// S_j = K_j Q^T and, while the matrix core works through them, evaluates the exponentials
+// of stage j-1 on the vector ALUs (scheduling groups interleave the two instruction
+// streams); it then accumulates O += V_{j-1}^T P_{j-1}^T. K_{j+1} is DMA'd during
+// iteration j; V_j is loaded into registers at the start of iteration j and written as a
+// V^T tile at its end, ready for iteration j+1. One barrier per iteration.
+// ---------------------------------------------------------------------------------------
+
+// First half of the online-softmax step for the two 32-key blocks of a stage: exclusion of
+// disallowed pairs (-inf), row maximum, lazy rescale of l and O. Returns the exponent
+// offset the stage's weights are taken against.
+template <int D>
+__device__ __forceinline__ float stage_max(f32x16 (&s)[2], bool need_mask, int pq, int kpos0,
+                                           const SeqGeom& g, int mode, int window, float c2,
+                                           float& m_run, float& l_run, f32x16 (&o)[D / 32],
+                                           int lane) {
+  const int hg = lane >> 5;
+  if (need_mask) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = pair_allowed(pq, kpos0 + 32 * kb + key_of_reg(r, hg), g, mode, window);
+        s[kb][r] = ok ? s[kb][r] : neg_inf();
+      }
+  }
+  float mx = neg_inf();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = max_halves(mx);
+  const float mt = (mx == neg_inf()) ? neg_inf() : mx * c2;
+  const bool grow = mt > m_run + RESCALE_THRESHOLD;
+  if (__any(grow)) {
+    const float m_new = grow ? mt : m_run;
+    const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;  // 0 if nothing seen yet
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    m_run = m_new;
+  }
+  return (m_run == neg_inf()) ? 0.0f : m_run;
+}
+
+// Second half: P = exp2(c2 S - base) as the bf16 PV operand; returns the fp32 sum of the
+// unrounded weights. Excluded pairs hold -inf and give exactly 0 (c2 > 0).
+template <int D>
+__device__ __forceinline__ float stage_exp(f32x16 (&s)[2], typename Mma<__bf16, D>::PPack (&pk)[2],
+                                           float c2, float base) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(fmaf(s[kb][r], c2, -base));
+  return Mma<__bf16, D>::pack_p(s[0], pk[0]) + Mma<__bf16, D>::pack_p(s[1], pk[1]);
+}
+
+// S_new = K_tile Q^T for both 32-key blocks, with the exponentials of the previous stage
+// (s_old -> pk) interleaved: per MFMA one operand read (PF ahead) and ~7 VALU instructions.
+template <int D>
+__device__ __forceinline__ float qk_with_exp(f32x16 (&sn)[2], const char* kt,
+                                             const bf16x8 (&qr)[D / 16],
+                                             const typename Mma<__bf16, D>::Offsets& of,
+                                             f32x16 (&so)[2],
+                                             typename Mma<__bf16, D>::PPack (&pk)[2], float c2,
+                                             float base) {
+  typedef Mma<__bf16, D> M;
+  constexpr int ROWB = M::ROWB, N = 2 * M::QREGS, PF = M::PF;
+  bf16x8 a[N];
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    a[i] = *reinterpret_cast<const bf16x8*>(kt + (i & 1) * 32 * ROWB + of.k[i >> 1]);
+  sn[0] = f32x16{};
+  sn[1] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + PF < N) {
+      const int j = i + PF;
+      a[j] = *reinterpret_cast<const bf16x8*>(kt + (j & 1) * 32 * ROWB + of.k[j >> 1]);
+    }
+    sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qr[i >> 1], sn[i & 1], 0, 0, 0);
+  }
+  const float sum = stage_exp<D>(so, pk, c2, base);
+  constexpr int NV = (112 + N - 1) / N;  // fma + exp per weight, bf16 packs, fp32 sums
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+  return sum;
+}
+
+// Loop-invariant operands and geometry of one pipelined prefill wave.
+template <int D>
+struct PipeCtx {
+  typedef Mma<__bf16, D> M;
+  const FwdParams& p;
+  const SeqGeom& g;
+  const bf16x8 (&qr)[D / 16];
+  const typename M::Offsets& of;
+  DmaStager<2 * D, FWD_BN, 4>& dma;
+  VtStager<D, FWD_BN>& vst;
+  const char* kg;
+  const char* vg;
+  uint32_t rstride;
+  int nst, kstart, wp0, wp1, pq, lane;
+};
+
+// Running state: O accumulator, exponent offset, partial denominator.
+template <int D>
+struct PipeRun {
+  f32x16 o[D / 32];
+  float m_run, l_run;
+  bool mask_prev;  // the stage whose weights are pending needs per-lane masking
+};
+
+// Steady iteration j (0 < j < nst): stage j's K in kbuf[B] (B = j % 2), stage j-1's scores
+// in `so`, its V^T in vbuf[B ^ 1]; stage j's scores go to `sn`.
+template <int D, int B>
+__device__ __forceinline__ void prefill_steady(const PipeCtx<D>& c, PipeRun<D>& r, int j,
+                                               f32x16 (&sn)[2], f32x16 (&so)[2],
+                                               char* const (&kbuf)[2], char* const (&vbuf)[2]) {
+  typedef Mma<__bf16, D> M;
+  constexpr int BN = FWD_BN;
+  const int kcur = c.kstart + j * BN;
+  if (j + 1 < c.nst)
+    c.dma.issue(c.kg + (size_t)(kcur + BN) * c.rstride, c.g.len_k - kcur - BN, c.rstride,
+                kbuf[B ^ 1]);
+  const float base = stage_max<D>(so, r.mask_prev, c.pq, kcur - BN, c.g, c.p.mode, c.p.window,
+                                  c.p.c2, r.m_run, r.l_run, r.o, c.lane);
+  typename M::PPack pk[2];
+  r.l_run += qk_with_exp<D>(sn, kbuf[B], c.qr, c.of, so, pk, c.p.c2, base);
+  // V_j is loaded after the QK/exp phase (whose register footprint is the largest) and
+  // lands during the PV phase.
+  c.vst.issue(c.vg + (size_t)kcur * c.rstride, c.g.len_k - kcur, c.rstride);
+  M::pv2(r.o, pk, vbuf[B ^ 1], c.of);
+  r.mask_prev = block_class(c.wp0, c.wp1, kcur, kcur + BN, c.g, c.p.mode, c.p.window) != 2;
+  wait_vmem();
+  c.vst.write(vbuf[B]);
+  __syncthreads();
+}
+
+// Last step: weights and PV of stage nst - 1 (scores in `so`, V^T in vbuf[B]).
+template <int D, int B>
+__device__ __forceinline__ void prefill_tail(const PipeCtx<D>& c, PipeRun<D>& r,
+                                             f32x16 (&so)[2], char* const (&vbuf)[2]) {
+  typedef Mma<__bf16, D> M;
+  const int klast = c.kstart + (c.nst - 1) * FWD_BN;
+  const float base = stage_max<D>(so, r.mask_prev, c.pq, klast, c.g, c.p.mode, c.p.window,
+                                  c.p.c2, r.m_run, r.l_run, r.o, c.lane);
+  typename M::PPack pk[2];
+  r.l_run += stage_exp<D>(so, pk, c.p.c2, base);
+  M::pv2(r.o, pk, vbuf[B], c.of);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
+  typedef Mma<__bf16, D> M;
+  typedef VtStager<D, FWD_BN> VS;
+  constexpr int BM = FWD_BM, BN = FWD_BN, ROWB = M::ROWB, KTILE = BN * ROWB;
+  static_assert(2 * (KTILE + VS::TILE_BYTES) <= LDS_BYTES / 2, "two workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) char kbuf0[KTILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[KTILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[VS::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[VS::TILE_BYTES];
+  char* const kbuf[2] = {kbuf0, kbuf1};
+  char* const vbuf[2] = {vbuf0, vbuf1};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  int h, s, tile;
+  SeqGeom g;
+  if (!prefill_tile<BM>(p, h, s, tile, g)) return;
+  const int p0 = tile * BM, p1 = min(p0 + BM, g.len_q);
+  const int kvh = h / p.group;
+  const int wp0 = p0 + 32 * wave, wp1 = min(wp0 + 32, p1);
+  const int pq = wp0 + (lane & 31);
+  const bool qvalid = pq < wp1;
+  bf16x8 qr[M::QREGS];
+  const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)(g.q_start + pq) * p.hq + h) * D;
+  M::load_q(qr, qrow, qvalid, p.neg != 0, lane);
+  const typename M::Offsets of = M::offsets(lane);
+
+  int klo, khi;
+  visible_keys(p0, p1, g, p.mode, p.window, klo, khi);
+  const int kstart = (klo / BN) * BN;
+  const int nst = khi > klo ? (khi - kstart + BN - 1) / BN : 0;
+
+  const uint32_t rstride = (uint32_t)(p.hkv * D * 2);
+  const char* kg = static_cast<const char*>(p.k) + ((size_t)g.k_start * p.hkv + kvh) * D * 2;
+  const char* vg = static_cast<const char*>(p.v) + ((size_t)g.k_start * p.hkv + kvh) * D * 2;
+  DmaStager<ROWB, BN, 4> dma;
+  dma.init(wave, lane, rstride);
+  VS vst;
+  vst.init(tid, rstride);
+
+  PipeRun<D> r;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) r.o[db] = f32x16{};
+  r.m_run = neg_inf();
+  r.l_run = 0.0f;
+  r.mask_prev = true;
+  const PipeCtx<D> c{p, g, qr, of, dma, vst, kg, vg, rstride, nst, kstart, wp0, wp1, pq, lane};
+  f32x16 sa[2], sb[2];  // scores of even / odd stages
+
+  if (nst > 0) {
+    dma.issue(kg + (size_t)kstart * rstride, g.len_k - kstart, rstride, kbuf0);
+    wait_vmem();
+    __syncthreads();
+    // Stage 0: scores only.
+    if (nst > 1)
+      dma.issue(kg + (size_t)(kstart + BN) * rstride, g.len_k - kstart - BN, rstride, kbuf1);
+    sa[0] = f32x16{};
+    sa[1] = f32x16{};
+    M::qk2(sa, kbuf0, qr, of);
+    vst.issue(vg + (size_t)kstart * rstride, g.len_k - kstart, rstride);
+    r.mask_prev = block_class(wp0, wp1, kstart, kstart + BN, g, p.mode, p.window) != 2;
+    wait_vmem();
+    vst.write(vbuf0);
+    __syncthreads();
+    int j = 1;
+    for (; j + 1 < nst; j += 2) {
+      prefill_steady<D, 1>(c, r, j, sb, sa, kbuf, vbuf);
+      prefill_steady<D, 0>(c, r, j + 1, sa, sb, kbuf, vbuf);
+    }
+    if (j < nst) {
+      prefill_steady<D, 1>(c, r, j, sb, sa, kbuf, vbuf);
+      prefill_tail<D, 1>(c, r, sb, vbuf);
+    } else {
+      prefill_tail<D, 0>(c, r, sa, vbuf);
+    }
+  }
+
+  // Epilogue: O = acc / l (exactly +0.0 for rows that saw no allowed key), natural-log LSE.
+  const float lt = sum_halves(r.l_run);
+  const bool nonempty = lt > 0.0f;
+  const float inv = nonempty ? 1.0f / lt : 0.0f;
+  if (qvalid) {
+    __bf16* orow = static_cast<__bf16*>(p.out) + ((size_t)(g.q_start + pq) * p.hq + h) * D;
+    const int hg = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = db * 32 + 8 * a + 4 * hg;
+        M::store4(orow + d, nonempty ? r.o[db][4 * a] * inv : 0.0f,
+                  nonempty ? r.o[db][4 * a + 1] * inv : 0.0f,
+                  nonempty ? r.o[db][4 * a + 2] * inv : 0.0f,
+                  nonempty ? r.o[db][4 * a + 3] * inv : 0.0f);
+      }
+    if (hg == 0)
+      p.lse[(size_t)h * p.total_q + g.q_start + pq] =
+          nonempty ? (r.m_run + fast_log2(lt)) * LN2 : neg_inf();
   }
 }
 
@@ -490,7 +829,9 @@ static FwdParams make_params(const FwdArgs& a) {
   p.hkv = a.hkv;
   p.group = a.hq / a.hkv;
   const double c2 = (a.scale < 0 ? -(double)a.scale : (double)a.scale) * 1.4426950408889634;
-  p.c2 = (float)c2;
+  // A zero scale runs as the smallest normal float: every allowed weight is then exactly 1
+  // (|s| * 2^-126 rounds away inside exp2), and -inf * c2 stays -inf for excluded pairs.
+  p.c2 = std::max((float)c2, 1.17549435e-38f);
   p.neg = a.scale < 0;
   p.mode = a.mode;
   p.window = a.window;
@@ -499,7 +840,16 @@ static FwdParams make_params(const FwdArgs& a) {
   return p;
 }
 
+// Every sequence has max_q queries and max_k keys exactly when the totals say so (each
+// length is at most its maximum).
+bool equal_lengths(const FwdArgs& a) {
+  return a.max_q > 0 && (long)a.total_q == (long)a.num_seqs * a.max_q &&
+         (long)a.total_k == (long)a.num_seqs * a.max_k;
+}
+
 int fwd_prefill_grid(const FwdArgs& a) {
+  const long ntiles = (a.max_q + FWD_BM - 1) / FWD_BM;
+  if (equal_lengths(a)) return (int)(ntiles * a.num_seqs * a.hq);
   const long nslots = (long)a.total_q / FWD_BM + a.num_seqs;
   const long nlogical = nslots * a.hq;
   return (int)(((nlogical + 7) / 8) * 8);
@@ -510,8 +860,15 @@ static hipError_t prefill_typed(const FwdArgs& a, hipStream_t st) {
   FwdParams p = make_params(a);
   p.nslots = a.total_q / FWD_BM + a.num_seqs;
   p.nlogical = p.nslots * a.hq;
+  if (equal_lengths(a)) {
+    p.uni_ntiles = (a.max_q + FWD_BM - 1) / FWD_BM;
+    p.npairs = a.num_seqs * a.hq;
+  }
   const int grid = fwd_prefill_grid(a);
-  hipLaunchKernelGGL((fwd_prefill_kernel<T, D>), dim3(grid), dim3(256), 0, st, p);
+  if constexpr (std::is_same<T, __bf16>::value)
+    hipLaunchKernelGGL((fwd_prefill_bf16_kernel<D>), dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_prefill_kernel<T, D>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -39,6 +39,9 @@ constexpr int FWD_BN = 64;
 constexpr int SPLITK_STAGE = 128;
 constexpr int SPLITK_MAX_ROWS = 64;
 
+// True when every sequence has exactly max_q queries and max_k keys; the prefill then
+// orders its tiles heaviest first across all (sequence, head) pairs.
+bool equal_lengths(const FwdArgs& a);
 int fwd_prefill_grid(const FwdArgs& a);
 hipError_t launch_fwd_prefill(const FwdArgs& a, hipStream_t stream);
 

@@ -108,6 +108,49 @@ def test_splitk_decode_shapes(dtype, mode, window, nq, group):
 
 
 # ----------------------------------------------------------------------------------------
+# equal-length batches: the prefill enumerates tiles largest-first across (sequence, head)
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lq,lk,mode,window", [
+    (300, 450, 2, 0), (300, 450, 1, 0), (450, 300, 2, 0), (450, 300, 1, 0), (257, 257, 0, 0),
+    (384, 384, 1, 100), (200, 600, 2, 129), (1, 1, 1, 0)])
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (8, 8), (12, 3)])
+def test_equal_length_batches(lq, lk, mode, window, hq, hkv):
+    """Every sequence of the pack has the same lengths (ragged tails inside the last tile),
+    head counts that are and are not multiples of 8; against the oracle, and bitwise equal
+    to the same sequences preceded by a one-token sequence (which forces the slot order)."""
+    import exact_attention_tiled_amd as eat
+    import torch
+    nseq = 3
+    w = wl.random_workload((14, lq, lk, mode, hq), [lq] * nseq, [lk] * nseq, hq, hkv, 64,
+                           "bf16", mode, window, name="equal", v_offsets=True)
+    print(f"equal-length lq={lq} lk={lk} mode={mode} window={window} hq={hq} hkv={hkv}",
+          flush=True)
+    t = to_device(w)
+    plan = eat.attn_describe_plan(t["q"], t["k"], t["cu_q"], w.max_seqlen_q, w.max_seqlen_k,
+                                  w.mask_mode, w.window)
+    assert "order=largest_first" in plan, plan
+    out, lse = run_fwd(w, t, path=PREFILL)
+    check_fwd(w, out, lse, *_oracle(w), "equal-length")
+    if lq == 1 and lk == 1:
+        return  # a one-token prefix would keep the batch equal-length
+    # The same pack after a one-token sequence: not equal-length, so the slot order runs.
+    q1 = torch.cat([t["q"][:1], t["q"]])
+    k1 = torch.cat([t["k"][:1], t["k"]])
+    v1 = torch.cat([t["v"][:1], t["v"]])
+    cu_q1 = torch.cat([t["cu_q"][:1], t["cu_q"] + 1])
+    cu_k1 = torch.cat([t["cu_k"][:1], t["cu_k"] + 1])
+    plan1 = eat.attn_describe_plan(q1, k1, cu_q1, w.max_seqlen_q, w.max_seqlen_k, w.mask_mode,
+                                   w.window)
+    assert "order=slots" in plan1, plan1
+    out1, lse1 = eat.attn_fwd(q1, k1, v1, cu_q1, cu_k1, w.max_seqlen_q, w.max_seqlen_k, w.scale,
+                              w.mask_mode, w.window, path=PREFILL)
+    torch.cuda.synchronize()
+    assert torch.equal(out1[1:].view(torch.int16), out.view(torch.int16))
+    assert torch.equal(lse1[:, 1:], lse)
+
+
+# ----------------------------------------------------------------------------------------
 # bit-exact behaviour: empty rows, masked K/V perturbation, packing, determinism
 # ----------------------------------------------------------------------------------------
 
