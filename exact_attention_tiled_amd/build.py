@@ -4,7 +4,10 @@
 
 hipcc cross-compiles for gfx950 without a GPU present. Packed-fp32 instruction selection is
 switched off for all device code (-packed-fp32-ops); fp32 atomics use the hardware
-instructions (-munsafe-fp-atomics; device memory from hipMalloc is coarse-grained).
+instructions (-munsafe-fp-atomics; device memory from hipMalloc is coarse-grained). MFMA
+results stay in architectural VGPRs (-amdgpu-mfma-vgpr-form): every accumulator is also
+read by vector instructions (softmax, rescale), and accumulation registers would cost a
+copy each way.
 """
 from __future__ import annotations
 
@@ -33,6 +36,7 @@ def hipcc() -> str:
 def compile_command(out: str = LIB_PATH) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-munsafe-fp-atomics", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"] + \
         [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out]
 

@@ -73,7 +73,8 @@ int make_plan(int32_t num_seqs, int32_t total_q, int32_t max_q, int32_t max_k, i
   nsb = std::max<long>(1, (max_k + chunk - 1) / chunk);
   plan->nsb = (int)nsb;
   plan->chunk = (int)chunk;
-  plan->workspace = attn::splitk_workspace_bytes((int)nsb * 4, total_q, hq, d);
+  plan->workspace = attn::splitk_workspace_bytes(
+      (int)nsb * attn::splitk_partials_per_chunk((int)rows), total_q, hq, d);
   return ATTN_OK;
 }
 
@@ -288,7 +289,8 @@ int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32
                   "path=splitk dtype=%s d=%d stage=%d rows_per_kvhead<=%d blocks_per_kvhead=%d "
                   "chunk=%d partials=%d grid=%ld workspace=%zu version=%d",
                   dt, d, attn::SPLITK_STAGE, (hq / hkv) * max_q, plan.nsb, plan.chunk,
-                  plan.nsb * 4, (long)num_seqs * hkv * plan.nsb, plan.workspace, ATTN_VERSION);
+                  plan.nsb * attn::splitk_partials_per_chunk((hq / hkv) * max_q),
+                  (long)num_seqs * hkv * plan.nsb, plan.workspace, ATTN_VERSION);
   }
   return ATTN_OK;
 }

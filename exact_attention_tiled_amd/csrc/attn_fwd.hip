@@ -451,13 +451,11 @@ __device__ __forceinline__ void prefill_steady(const PipeCtx<D>& c, PipeRun<D>& 
   if (j + 1 < c.nst)
     c.dma.issue(c.kg + (size_t)(kcur + BN) * c.rstride, c.g.len_k - kcur - BN, c.rstride,
                 kbuf[B ^ 1]);
+  c.vst.issue(c.vg + (size_t)kcur * c.rstride, c.g.len_k - kcur, c.rstride);
   const float base = stage_max<D>(so, r.mask_prev, c.pq, kcur - BN, c.g, c.p.mode, c.p.window,
                                   c.p.c2, r.m_run, r.l_run, r.o, c.lane);
   typename M::PPack pk[2];
   r.l_run += qk_with_exp<D>(sn, kbuf[B], c.qr, c.of, so, pk, c.p.c2, base);
-  // V_j is loaded after the QK/exp phase (whose register footprint is the largest) and
-  // lands during the PV phase.
-  c.vst.issue(c.vg + (size_t)kcur * c.rstride, c.g.len_k - kcur, c.rstride);
   M::pv2(r.o, pk, vbuf[B ^ 1], c.of);
   r.mask_prev = block_class(c.wp0, c.wp1, kcur, kcur + BN, c.g, c.p.mode, c.p.window) != 2;
   wait_vmem();
@@ -578,73 +576,78 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
   }
 }
 
-// Running state of one split-K wave (NRB blocks of 32 query rows) and its step over its
-// 32-key block of one 128-key stage.
-template <typename T, int D, int NRB>
+// Running state of one split-K wave: one block of 32 query rows over KBW consecutive
+// 32-key blocks of each stage.
+template <typename T, int D, int KBW>
 struct SplitkWave {
   typedef Mma<T, D> M;
-  f32x16 o[NRB][D / 32];
-  float m_run[NRB], l_run[NRB];
+  f32x16 o[D / 32];
+  float m_run, l_run;
 
   __device__ __forceinline__ void init() {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[rb][db] = f32x16{};
-      m_run[rb] = neg_inf();
-      l_run[rb] = 0.0f;
-    }
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    m_run = neg_inf();
+    l_run = 0.0f;
   }
 
-  __device__ __forceinline__ void stage(const char* buf, int k0, int klo, int khi, int R, int wave,
-                                        const int (&pq)[NRB], const SeqGeom& g,
+  // Keys [kw0, kw0 + 32 KBW) of a stage, staged at kt / vt (row 0 = key kw0); rows
+  // [rlo, rhi) of the group's G * len_q (position, head) rows; only keys in [klo, khi)
+  // (this workgroup's chunk) count.
+  __device__ __forceinline__ void stage(const char* kt, const char* vt, int kw0, int klo, int khi,
+                                        int rlo, int rhi, int pq, const SeqGeom& g,
                                         const FwdParams& p,
-                                        const typename M::QOperand (&qr)[NRB][M::QREGS],
+                                        const typename M::QOperand (&qr)[M::QREGS],
                                         const typename M::Offsets& of, int lane) {
-    constexpr int ROWB = M::ROWB, TILE = SPLITK_STAGE * ROWB;
+    constexpr int ROWB = M::ROWB;
     const int G = p.group;
-    const int kw = k0 + 32 * wave;  // this wave's key block
-    // A key outside this block's chunk belongs to a neighbouring chunk's partial.
-    const int cw0 = max(kw, klo), cw1 = min(kw + 32, khi);
+    const int cw0 = max(kw0, klo), cw1 = min(kw0 + 32 * KBW, khi);
+    const int cls = (rhi <= rlo || cw1 <= cw0)
+                        ? 0
+                        : block_class(rlo / G, (rhi - 1) / G + 1, kw0, kw0 + 32 * KBW, g, p.mode,
+                                      p.window);
+    if (cls == 0) return;
+    // A key outside the chunk belongs to a neighbouring chunk's partial.
+    const bool clip = cw0 != kw0 || cw1 != kw0 + 32 * KBW;
+    f32x16 sacc[KBW];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int rlo = rb * 32, rhi = min(R, rb * 32 + 32);
-      const int cls = (rhi <= rlo || cw1 <= cw0)
-                          ? 0
-                          : block_class(rlo / G, (rhi - 1) / G + 1, kw, kw + 32, g, p.mode, p.window);
-      if (cls == 0) continue;
-      const bool clip = cw0 != kw || cw1 != kw + 32;
-      f32x16 sacc[1];
-      sacc[0] = f32x16{};
-      M::qk(sacc[0], buf + 32 * wave * ROWB, qr[rb], of, lane);
-      if (clip) {
-        const int hg = lane >> 5;
+    for (int i = 0; i < KBW; ++i) {
+      sacc[i] = f32x16{};
+      M::qk(sacc[i], kt + 32 * i * ROWB, qr, of, lane);
+    }
+    if (clip) {
+      const int hg = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < KBW; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = kw + key_of_reg(r, hg);
-          sacc[0][r] = ((kk >= cw0) & (kk < cw1)) ? sacc[0][r] : neg_inf();
+          const int kk = kw0 + 32 * i + key_of_reg(r, hg);
+          sacc[i][r] = ((kk >= cw0) & (kk < cw1)) ? sacc[i][r] : neg_inf();
         }
-      }
-      typename M::PPack pk[1];
-      softmax_step<M, 1, D>(sacc, pk, cls == 1 || clip, pq[rb], kw, g, p.mode, p.window, p.c2,
-                            m_run[rb], l_run[rb], o[rb], lane);
-      M::pv(o[rb], pk[0], buf + TILE + 32 * wave * ROWB, of, lane);
     }
+    typename M::PPack pk[KBW];
+    softmax_step<M, KBW, D>(sacc, pk, cls == 1 || clip, pq, kw0, g, p.mode, p.window, p.c2, m_run,
+                            l_run, o, lane);
+#pragma unroll
+    for (int i = 0; i < KBW; ++i) M::pv(o, pk[i], vt + 32 * i * ROWB, of, lane);
   }
 };
 
 // ---------------------------------------------------------------------------------------
 // Split-K decode: one workgroup = one (sequence, K/V head, key chunk). Its rows are the
-// G * len_q (query head, query position) pairs of the group, shared by the 4 waves, so
-// every K/V byte is read once for the whole group. Each 128-key stage gives each wave its
-// own 32-key block; each wave keeps its own running state and writes its own partial
-// (O_e normalised, LSE_e) with e = chunk * 4 + wave. The combine kernel merges partials.
+// G * len_q (query head, query position) pairs of the group, so every K/V byte is read
+// once for the whole group. With NRB row blocks of 32, wave w owns row block w % NRB and
+// KBW = NRB consecutive 32-key blocks of every 128-key stage (the waves sharing a row
+// block split the stage's keys); each wave keeps its own running state and writes its own
+// partial (O_e normalised, LSE_e), e = chunk * (4 / NRB) + w / NRB. The combine kernel
+// merges the partials of each row.
 // ---------------------------------------------------------------------------------------
 template <typename T, int D, int NRB>
 __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
   typedef Mma<T, D> M;
   constexpr int BN = SPLITK_STAGE, ROWB = M::ROWB;
   constexpr int TILE = BN * ROWB;
+  constexpr int KW = 4 / NRB, KBW = NRB;  // waves per row block, key blocks per wave
   static_assert(2 * 2 * TILE <= LDS_BYTES, "two K/V stages must fit in LDS");
   __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];
@@ -659,18 +662,17 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
   const int R = G * g.len_q;
   if (R == 0) return;
 
-  // Rows: r = position * G + head-in-group.
-  typename M::QOperand qr[NRB][M::QREGS];
-  int pq[NRB];
-  bool rvalid[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int r = rb * 32 + (lane & 31);
-    rvalid[rb] = r < R;
-    pq[rb] = rvalid[rb] ? r / G : 0;
-    const int h = kvh * G + (rvalid[rb] ? r % G : 0);
-    const T* qrow = static_cast<const T*>(p.q) + ((size_t)(g.q_start + pq[rb]) * p.hq + h) * D;
-    M::load_q(qr[rb], qrow, rvalid[rb], p.neg != 0, lane);
+  // This wave's rows: r = position * G + head-in-group, r in [rlo, rhi).
+  const int rb = wave % NRB, kwi = wave / NRB;
+  const int rlo = rb * 32, rhi = min(R, rlo + 32);
+  const int r = rlo + (lane & 31);
+  const bool rvalid = r < R;
+  const int pq = rvalid ? r / G : 0;
+  typename M::QOperand qr[M::QREGS];
+  {
+    const int h = kvh * G + (rvalid ? r % G : 0);
+    const T* qrow = static_cast<const T*>(p.q) + ((size_t)(g.q_start + pq) * p.hq + h) * D;
+    M::load_q(qr, qrow, rvalid, p.neg != 0, lane);
   }
   const typename M::Offsets of = M::offsets(lane);
 
@@ -687,7 +689,9 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
   DmaStager<ROWB, BN, 4> dma;
   dma.init(wave, lane, rstride);
 
-  SplitkWave<T, D, NRB> st;
+  // This wave's key blocks start at block kwi * KBW of each stage.
+  const int woff = 32 * kwi * KBW;
+  SplitkWave<T, D, KBW> st;
   st.init();
   if (nst > 0) {
     dma.issue(kb0 + (size_t)kstart * rstride, g.len_k - kstart, rstride, buf0);
@@ -701,7 +705,8 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
       dma.issue(kb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, buf1);
       dma.issue(vb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, buf1 + TILE);
     }
-    st.stage(buf0, k0, klo, khi, R, wave, pq, g, p, qr, of, lane);
+    st.stage(buf0 + woff * ROWB, buf0 + TILE + woff * ROWB, k0 + woff, klo, khi, rlo, rhi, pq, g,
+             p, qr, of, lane);
     wait_vmem();
     __syncthreads();
     if (it + 1 < nst) {
@@ -709,26 +714,21 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
         dma.issue(kb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, buf0);
         dma.issue(vb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, buf0 + TILE);
       }
-      st.stage(buf1, k0 + BN, klo, khi, R, wave, pq, g, p, qr, of, lane);
+      st.stage(buf1 + woff * ROWB, buf1 + TILE + woff * ROWB, k0 + BN + woff, klo, khi, rlo, rhi,
+               pq, g, p, qr, of, lane);
       wait_vmem();
       __syncthreads();
     }
   }
-  f32x16 (&o)[NRB][D / 32] = st.o;
-  float (&m_run)[NRB] = st.m_run;
-  float (&l_run)[NRB] = st.l_run;
 
-  // Partial of split e: normalised O_e (fp32) and LSE_e; empty -> O_e = 0, LSE_e = -inf.
-  const int e = sigma * 4 + wave;
+  // Partial e of this wave: normalised O_e (fp32) and LSE_e; empty -> O_e = 0, LSE_e = -inf.
+  const int e = sigma * KW + kwi;
   const int hg = lane >> 5;
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const float lt = sum_halves(l_run[rb]);
-    const bool nonempty = lt > 0.0f;
-    const float inv = nonempty ? 1.0f / lt : 0.0f;
-    if (!rvalid[rb]) continue;
-    const int r = rb * 32 + (lane & 31);
-    const int t = g.q_start + pq[rb];
+  const float lt = sum_halves(st.l_run);
+  const bool nonempty = lt > 0.0f;
+  const float inv = nonempty ? 1.0f / lt : 0.0f;
+  if (rvalid) {
+    const int t = g.q_start + pq;
     const int h = kvh * G + r % G;
     float* dst = p.part_o + (((size_t)e * p.total_q + t) * p.hq + h) * D;
 #pragma unroll
@@ -737,12 +737,12 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
       for (int a = 0; a < 4; ++a) {
         const int d = db * 32 + 8 * a + 4 * hg;
         *reinterpret_cast<f32x4*>(dst + d) =
-            f32x4{nonempty ? o[rb][db][4 * a] * inv : 0.0f, nonempty ? o[rb][db][4 * a + 1] * inv : 0.0f,
-                  nonempty ? o[rb][db][4 * a + 2] * inv : 0.0f, nonempty ? o[rb][db][4 * a + 3] * inv : 0.0f};
+            f32x4{nonempty ? st.o[db][4 * a] * inv : 0.0f, nonempty ? st.o[db][4 * a + 1] * inv : 0.0f,
+                  nonempty ? st.o[db][4 * a + 2] * inv : 0.0f, nonempty ? st.o[db][4 * a + 3] * inv : 0.0f};
       }
     if (hg == 0)
       p.part_lse[((size_t)e * p.hq + h) * p.total_q + t] =
-          nonempty ? (m_run[rb] + fast_log2(lt)) * LN2 : neg_inf();
+          nonempty ? (st.m_run + fast_log2(lt)) * LN2 : neg_inf();
   }
 }
 
@@ -877,6 +877,8 @@ hipError_t launch_fwd_prefill(const FwdArgs& a, hipStream_t st) {
   return a.d == 64 ? prefill_typed<float, 64>(a, st) : prefill_typed<float, 128>(a, st);
 }
 
+int splitk_partials_per_chunk(int rows) { return rows <= 32 ? 4 : 2; }
+
 size_t splitk_workspace_bytes(int nsplit_eff, int total_q, int hq, int d) {
   const size_t o = (size_t)nsplit_eff * total_q * hq * d * sizeof(float);
   const size_t l = (size_t)nsplit_eff * hq * total_q * sizeof(float);
@@ -888,12 +890,12 @@ static hipError_t splitk_typed(const FwdArgs& a, int nsb, int chunk, void* ws, h
   FwdParams p = make_params(a);
   p.blocks_per_kvh = nsb;
   p.chunk = chunk;
-  p.nsplit = nsb * 4;
+  const int rows = (a.hq / a.hkv) * a.max_q;
+  p.nsplit = nsb * splitk_partials_per_chunk(rows);
   const size_t obytes = (size_t)p.nsplit * a.total_q * a.hq * D * sizeof(float);
   p.part_o = static_cast<float*>(ws);
   p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + ((obytes + 255) / 256) * 256);
   const int grid = a.num_seqs * a.hkv * nsb;
-  const int rows = (a.hq / a.hkv) * a.max_q;
   if (rows <= 32)
     hipLaunchKernelGGL((fwd_splitk_kernel<T, D, 1>), dim3(grid), dim3(256), 0, st, p);
   else
