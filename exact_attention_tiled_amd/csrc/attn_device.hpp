@@ -319,6 +319,14 @@ struct VtStager {
 // publishes an LDS stage).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N vector-memory operations of this thread are outstanding (loads
+// complete in issue order): the N most recent loads may stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_leave() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------------------------------
 // Element-type specific contractions on swizzled tiles. Key k of a 32-key block sits in
 // register r of lane half g = l / 32 with k = 8 * (r / 4) + 4 * g + (r % 4) (the

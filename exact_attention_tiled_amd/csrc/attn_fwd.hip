@@ -32,6 +32,7 @@ struct FwdParams {
   // lengths, tiles of `uni_ntiles` per sequence enumerated heaviest first (uni_ntiles > 0)
   int nslots, nlogical;
   int uni_ntiles, npairs;
+  int uni_lq, uni_lk;  // equal-length batch: every sequence's query / key length
   // split-K
   float* part_o;
   float* part_lse;
@@ -117,7 +118,12 @@ __device__ __forceinline__ bool prefill_tile(const FwdParams& p, int& h, int& s,
     s = pair / p.hq;
     const int hp = pair - s * p.hq;
     h = (hp % p.hkv) * p.group + hp / p.hkv;
-    g = load_geom(p.cu_q, p.cu_k, s, p.mode);
+    // Every length equals its maximum, so cu_seqlens[s] = s * length: no loads needed.
+    g.q_start = s * p.uni_lq;
+    g.k_start = s * p.uni_lk;
+    g.len_q = p.uni_lq;
+    g.len_k = p.uni_lk;
+    g.off = p.mode == MASK_BOTTOM_RIGHT ? p.uni_lk - p.uni_lq : 0;
     const int ntiles = (g.len_q + BM - 1) / BM;
     tile = p.uni_ntiles - 1 - rank;  // latest (heaviest under causal masks) tiles first
     return tile < ntiles;
@@ -526,16 +532,25 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
   f32x16 sa[2], sb[2];  // scores of even / odd stages
 
   if (nst > 0) {
+    // K_0, V_0 and K_1 are all requested before the first wait: the tile's start costs one
+    // memory round trip, not three.
     dma.issue(kg + (size_t)kstart * rstride, g.len_k - kstart, rstride, kbuf0);
-    wait_vmem();
+    vst.issue(vg + (size_t)kstart * rstride, g.len_k - kstart, rstride);
+    if (nst > 1) {
+      dma.issue(kg + (size_t)(kstart + BN) * rstride, g.len_k - kstart - BN, rstride, kbuf1);
+      // Wait for Q and K_0 only (this wave issued 4 V loads if it stages V, then K_1).
+      if (vst.active)
+        wait_vmem_leave<DmaStager<ROWB, BN, 4>::PER_WAVE + 4>();
+      else
+        wait_vmem_leave<DmaStager<ROWB, BN, 4>::PER_WAVE>();
+    } else {
+      wait_vmem();
+    }
     __syncthreads();
     // Stage 0: scores only.
-    if (nst > 1)
-      dma.issue(kg + (size_t)(kstart + BN) * rstride, g.len_k - kstart - BN, rstride, kbuf1);
     sa[0] = f32x16{};
     sa[1] = f32x16{};
     M::qk2(sa, kbuf0, qr, of);
-    vst.issue(vg + (size_t)kstart * rstride, g.len_k - kstart, rstride);
     r.mask_prev = block_class(wp0, wp1, kstart, kstart + BN, g, p.mode, p.window) != 2;
     wait_vmem();
     vst.write(vbuf0);
@@ -863,6 +878,8 @@ static hipError_t prefill_typed(const FwdArgs& a, hipStream_t st) {
   if (equal_lengths(a)) {
     p.uni_ntiles = (a.max_q + FWD_BM - 1) / FWD_BM;
     p.npairs = a.num_seqs * a.hq;
+    p.uni_lq = a.max_q;
+    p.uni_lk = a.max_k;
   }
   const int grid = fwd_prefill_grid(a);
   if constexpr (std::is_same<T, __bf16>::value)
