@@ -12,9 +12,10 @@ measured the same way and reported under "secondary".
 
 Protocol ("Attention Kernel Portability and Benchmarking", fourth and fifth sections):
 outputs are validated against the fp64 oracle on a sample before timing; warm-up calls;
-per-step HIP events on the launch stream give median / p10 / p90 / max; the K timed steps
-are bracketed by device synchronisation. The oracle is timed on the host cores on a bounded
-sample of the same workload (cpu_baseline).
+the K timed steps are bracketed by device synchronisation and by two HIP events on the
+launch stream (their mean gives ms per launch for the roofline); a second pass of K steps
+with per-step events gives median / p10 / p90 / max. The oracle is timed on the host cores
+on a bounded sample of the same workload (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -41,6 +42,7 @@ _CSRC = "exact_attention_tiled_amd/csrc/"
 # Sources that determine each kernel's machine code (a stored counter reading is only
 # reported while these are unchanged).
 KERNEL_SOURCES = {
+    "fwd_prefill_bf16_kernel": [_CSRC + "attn_device.hpp", _CSRC + "attn_fwd.hip", _CSRC + "attn_internal.h"],
     "fwd_prefill_kernel": [_CSRC + "attn_device.hpp", _CSRC + "attn_fwd.hip", _CSRC + "attn_internal.h"],
     "fwd_splitk_kernel": [_CSRC + "attn_device.hpp", _CSRC + "attn_fwd.hip", _CSRC + "attn_internal.h"],
     "bwd_main_kernel": [_CSRC + "attn_device.hpp", _CSRC + "attn_bwd.hip", _CSRC + "attn_internal.h"],
@@ -83,7 +85,7 @@ def bwd_bytes(w) -> int:
     return el * (w.q.size * 4 + w.k.size * 2 + w.v.size * 2) + 4 * w.hq * w.total_q
 
 
-def kernel_source_hash(kernel: str = "fwd_prefill_kernel") -> str:
+def kernel_source_hash(kernel: str = "fwd_prefill_bf16_kernel") -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
@@ -110,23 +112,34 @@ def stored_traffic(kernel: str, workload: str):
 # ----------------------------------------------------------------------------------------
 
 def time_steps(fn, steps: int, warmup: int):
+    """Warm-up, then K timed steps between two HIP events on the launch stream (bracketed by
+    device synchronisation): returns wall seconds, the mean event time per step, and the
+    per-step event times of a second, separate pass of K steps (distribution only: the
+    per-step event pairs add their own gaps, so they are kept out of the timed region)."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_ms = e0.elapsed_time(e1) / steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         starts[i].record(stream)
         fn()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    return wall, ms
+    ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return wall, mean_ms, ms
 
 
 def stats(ms):
@@ -206,8 +219,8 @@ def bench_forward(w, steps, warmup, validate=True):
     valid = validate_sample(w, out, lse) if validate else None
     if validate and not valid:
         raise SystemExit(f"validation against the oracle failed for {w.name}; not timing it")
-    wall, ms = time_steps(step, steps, warmup)
-    return {"wall_s": wall, "ms": ms, "plan": plan, "validated": valid}
+    wall, mean_ms, ms = time_steps(step, steps, warmup)
+    return {"wall_s": wall, "mean_ms": mean_ms, "ms": ms, "plan": plan, "validated": valid}
 
 
 def bench_train(w, steps, warmup):
@@ -241,10 +254,11 @@ def bench_train(w, steps, warmup):
     torch.cuda.synchronize()
     if not validate_sample(w, out, lse, grads=(dq, dk, dv)):
         raise SystemExit(f"validation against the oracle failed for {w.name}; not timing it")
-    wall, ms = time_steps(step, steps, warmup)
-    _, ms_f = time_steps(fwd, steps, 2)
-    _, ms_b = time_steps(bwd, steps, 2)
-    return {"wall_s": wall, "ms": ms, "ms_fwd": ms_f, "ms_bwd": ms_b}
+    wall, mean_ms, ms = time_steps(step, steps, warmup)
+    _, mean_f, ms_f = time_steps(fwd, steps, 2)
+    _, mean_b, ms_b = time_steps(bwd, steps, 2)
+    return {"wall_s": wall, "mean_ms": mean_ms, "ms": ms, "mean_fwd": mean_f, "ms_fwd": ms_f,
+            "mean_bwd": mean_b, "ms_bwd": ms_b}
 
 
 # ----------------------------------------------------------------------------------------
@@ -324,7 +338,7 @@ def main():
     if args.workload.startswith("decode"):
         r = bench_forward(w, args.steps, args.warmup)
         byts = fwd_bytes(w)
-        ms_avg = float(r["ms"].mean())
+        ms_avg = r["mean_ms"]
         value = byts * args.steps / r["wall_s"] / 1e9
         metric, unit = "attention decode GB/s (split-K forward)", "GB/s"
         roof = {"bound": "hbm", "achieved": byts / (ms_avg * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
@@ -333,22 +347,22 @@ def main():
     elif args.workload.startswith("train"):
         r = bench_train(w, args.steps, args.warmup)
         flops = 14.0 * w.d * pairs
-        ms_avg = float(r["ms"].mean())
+        ms_avg = r["mean_ms"]
         value = flops * args.steps / r["wall_s"] / 1e12
         metric, unit = "attention fwd+bwd TFLOP/s (causal-adjusted)", "TFLOP/s"
-        roof = {"bound": "mfma", "achieved": 10.0 * w.d * pairs / (float(r["ms_bwd"].mean()) * 1e-3) / 1e12,
+        roof = {"bound": "mfma", "achieved": 10.0 * w.d * pairs / (r["mean_bwd"] * 1e-3) / 1e12,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
         kernel = "bwd_main_kernel"
     else:
         r = bench_forward(w, args.steps, args.warmup)
         flops = 4.0 * w.d * pairs
-        ms_avg = float(r["ms"].mean())
+        ms_avg = r["mean_ms"]
         value = flops * args.steps / r["wall_s"] / 1e12
         metric, unit = "attention fwd TFLOP/s (causal-adjusted)", "TFLOP/s"
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
         roof = {"bound": "mfma", "achieved": flops / (ms_avg * 1e-3) / 1e12, "peak": peak,
                 "unit": "TFLOP/s"}
-        kernel = "fwd_prefill_kernel"
+        kernel = "fwd_prefill_bf16_kernel" if w.dtype == "bf16" else "fwd_prefill_kernel"
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(kernel, args.workload)
     roof["kernel"] = kernel
@@ -373,14 +387,14 @@ def main():
                 rr = bench_forward(sw, 20, 5)
                 b = fwd_bytes(sw)
                 sec.append({"workload": sw.name, "metric": "decode GB/s", "plan": rr["plan"],
-                            "value": b / (float(np.median(rr["ms"])) * 1e-3) / 1e9,
-                            "frac_of_hbm_peak": b / (float(np.median(rr["ms"])) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            "value": b / (rr["mean_ms"] * 1e-3) / 1e9,
+                            "frac_of_hbm_peak": b / (rr["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                             "step_stats": stats(rr["ms"])})
             else:
                 rr = bench_train(sw, 5, 2)
-                fwd_tf = 4.0 * sw.d * sp / (float(np.median(rr["ms_fwd"])) * 1e-3) / 1e12
-                bwd_tf = 10.0 * sw.d * sp / (float(np.median(rr["ms_bwd"])) * 1e-3) / 1e12
-                tot = 14.0 * sw.d * sp / (float(np.median(rr["ms"])) * 1e-3) / 1e12
+                fwd_tf = 4.0 * sw.d * sp / (rr["mean_fwd"] * 1e-3) / 1e12
+                bwd_tf = 10.0 * sw.d * sp / (rr["mean_bwd"] * 1e-3) / 1e12
+                tot = 14.0 * sw.d * sp / (rr["mean_ms"] * 1e-3) / 1e12
                 sec.append({"workload": sw.name, "metric": "fwd+bwd TFLOP/s", "value": tot,
                             "fwd_tflops": fwd_tf, "bwd_tflops": bwd_tf,
                             "frac_of_bf16_peak": tot / PEAK_BF16_TFLOPS,
