@@ -58,26 +58,28 @@ __device__ __forceinline__ void visible_queries(int k0, int k1, const SeqGeom& g
 // empty rows mapped to +inf (so every recomputed P of such a row is exactly 0). One wave
 // per (query token, query head).
 // ---------------------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
-                                                      const T* __restrict__ dout,
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ out,
+                                                      const __bf16* __restrict__ dout,
                                                       const float* __restrict__ lse, int total_q,
                                                       int hq, float* __restrict__ dvec,
                                                       float* __restrict__ lse2) {
-  const int lane = threadIdx.x & 63;
-  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // D / 8 lanes per (token, head) row, 16 bytes of O and dO each.
+  constexpr int LPR = D / 8;
+  const int tid = threadIdx.x;
+  const long item = (long)blockIdx.x * (256 / LPR) + tid / LPR;
   if (item >= (long)total_q * hq) return;
-  const int t = (int)(item / hq), h = (int)(item - (long)t * hq);
-  constexpr int PER = D / 64;
-  const size_t base = ((size_t)t * hq + h) * D + lane * PER;
+  const int sub = tid % LPR;
+  const size_t base = (size_t)item * D + sub * 8;
+  const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + base);
+  const bf16x8 g = *reinterpret_cast<const bf16x8*>(dout + base);
   float acc = 0.0f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    acc += (float)dout[base + i] * (float)out[base + i];
-  }
+  for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) {
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (sub == 0) {
+    const int t = (int)(item / hq), h = (int)(item - (long)t * hq);
     const size_t li = (size_t)h * total_q + t;
     dvec[li] = acc;
     const float l = lse[li];
@@ -422,7 +424,8 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   float* lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + vecb);
   const long items = (long)f.total_q * f.hq;
   if (items > 0) {
-    hipLaunchKernelGGL((bwd_pre_kernel<__bf16, D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st,
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((items + 256 / (D / 8) - 1) / (256 / (D / 8)))),
+                       dim3(256), 0, st,
                        static_cast<const __bf16*>(a.out), static_cast<const __bf16*>(a.dout), a.lse,
                        f.total_q, f.hq, dvec, lse2);
     hipError_t e = hipGetLastError();
