@@ -40,6 +40,16 @@ struct BwdParams {
   int nslots_q, nlogical_q;    // query-tile slots (dQ kernel)
 };
 
+// Query positions [lo, hi) that see key position pk (the transpose of key_interval): from
+// pk - off on with a causal mode, and only up to pk - off + window - 1 with a window; none
+// for keys at or beyond len_k.
+__device__ __forceinline__ void query_interval(int pk, const SeqGeom& g, int mode, int window,
+                                               int& lo, int& hi) {
+  lo = mode == MASK_NONE ? 0 : pk - g.off;
+  hi = (mode != MASK_NONE && window > 0) ? pk - g.off + window : 0x3fffffff;
+  if (pk >= g.len_k) hi = lo;
+}
+
 // Query positions [lo, hi) that can see any key position in [k0, k1) (k1 > k0).
 __device__ __forceinline__ void visible_queries(int k0, int k1, const SeqGeom& g, int mode,
                                                 int window, int& lo, int& hi) {
@@ -139,6 +149,9 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
   const int k0 = ktile * BWD_BN, k1 = min(k0 + BWD_BN, g.len_k);
   const int kw0 = k0 + 32 * kb;                   // this wave's first key position
   const int kj = kw0 + (lane & 31);               // this lane's key position
+  int kq_lo, kq_hi;                               // query positions that see key kj
+  query_interval(kj, g, p.mode, p.window, kq_lo, kq_hi);
+  const unsigned kq_width = kq_hi > kq_lo ? (unsigned)(kq_hi - kq_lo) : 0u;
 
   const uint32_t krs = (uint32_t)(p.hkv * D * 2);  // K/V row stride (bytes)
   const uint32_t qrs = (uint32_t)(p.hq * D * 2);   // Q/dO row stride (bytes)
@@ -211,6 +224,10 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
     const int qa = q0 + 32 * qh, qz = min(qa + 32, qend);
     const int cls = block_class(qa, qz, kw0, kw0 + 32, g, p.mode, p.window);
     if (cls != 0) {
+      // Register r holds query position qa + key_of_reg(r, l / 32): allowed iff it lies in
+      // this lane's key's query interval, one unsigned compare (every pair when cls == 2).
+      const unsigned qbase = (unsigned)(qa + 4 * hg - kq_lo);
+      const unsigned qwidth = cls == 2 ? 0xffffffffu : kq_width;
       typename M::PPack pp[1], pd[1];
       // S and dP with keys on the lanes: A = Q / dO rows, B = K / V rows (all from LDS).
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -231,7 +248,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * qh + key_of_reg(r, hg);
-        const bool ok = (cls == 2) | pair_allowed(q0 + row, kj, g, p.mode, p.window);
+        const bool ok = qbase + (unsigned)(8 * (r >> 2) + (r & 3)) < qwidth;
         const float pv = ok ? fast_exp2(fmaf(sacc[r], p.c, -lse2s[row])) : 0.0f;
         sacc[r] = pv;
         dpacc[r] = pv * (dpacc[r] - dvs[row]);
@@ -346,9 +363,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
+  int kv_lo, kv_hi;  // key positions this lane's query sees
+  key_interval(pq, g, p.mode, p.window, kv_lo, kv_hi);
+  const unsigned kv_width = kv_hi > kv_lo ? (unsigned)(kv_hi - kv_lo) : 0u;
   auto stage = [&](const char* kt, const char* vt, int k0) {
     const int cls = block_class(wp0, wp1, k0, k0 + BN, g, p.mode, p.window);
     if (cls == 0) return;
+    const unsigned kbase = (unsigned)(k0 + 4 * hg - kv_lo);
+    const unsigned kwidth = cls == 2 ? 0xffffffffu : kv_width;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -356,8 +378,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       M::qk(dpacc, vt + kb * 32 * ROWB, dor, of, lane);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * kb + key_of_reg(r, hg);
-        const bool ok = (cls == 2) | pair_allowed(pq, key, g, p.mode, p.window);
+        const bool ok = kbase + (unsigned)(32 * kb + 8 * (r >> 2) + (r & 3)) < kwidth;
         const float pv = ok ? fast_exp2(fmaf(sacc[r], p.c, -l2)) : 0.0f;
         sacc[r] = pv * (dpacc[r] - dvl);
       }

@@ -98,14 +98,44 @@ __device__ __forceinline__ SeqGeom load_geom(const int32_t* cu_q, const int32_t*
   return g;
 }
 
-// Is key position pk visible from query position pq? Out-of-range key lanes (pk >= len_k)
-// are excluded like any disallowed pair. Branch-free on purpose: callers turn the result
-// into a select, never into a divergent conditional store.
+// Key positions [lo, hi) visible from query position pq (none when hi <= lo). With
+// end = pq + off the aligned diagonal: every key of the sequence without a causal mode;
+// keys up to end with one; and only the `window` most recent of those, (end - window, end],
+// with a window. Keys at or beyond len_k (out-of-range tile lanes) are never visible.
+__device__ __forceinline__ void key_interval(int pq, const SeqGeom& g, int mode, int window,
+                                             int& lo, int& hi) {
+  const int end = pq + g.off;
+  hi = mode == MASK_NONE ? g.len_k : min(g.len_k, end + 1);
+  lo = (mode != MASK_NONE && window > 0) ? end - window + 1 : 0;
+}
+
+// Is key position pk >= 0 visible from query position pq? Branch-free on purpose: callers
+// turn the result into a select, never into a divergent conditional store.
 __device__ __forceinline__ bool pair_allowed(int pq, int pk, const SeqGeom& g, int mode,
                                              int window) {
-  const int end = pq + g.off;
-  const bool causal_ok = (pk <= end) & ((window <= 0) | (pk > end - window));
-  return (pk < g.len_k) & ((mode == MASK_NONE) | causal_ok);
+  int lo, hi;
+  key_interval(pq, g, mode, window, lo, hi);
+  return (pk >= lo) & (pk < hi);
+}
+
+// Per-lane exclusion for NK 32-key blocks in accumulator layout (register r of block kb
+// holds key kpos0 + 32 kb + 8 (r / 4) + 4 (l / 32) + r % 4 of this lane's query pq):
+// disallowed entries become -inf. lo <= pk < hi is one unsigned compare of pk - lo against
+// hi - lo, with pk - lo = base + (a compile-time constant per register).
+template <int NK>
+__device__ __forceinline__ void mask_blocks(f32x16 (&s)[NK], int pq, int kpos0, const SeqGeom& g,
+                                            int mode, int window, int lane) {
+  int lo, hi;
+  key_interval(pq, g, mode, window, lo, hi);
+  const int base = kpos0 + 4 * (lane >> 5) - lo;
+  const unsigned width = hi > lo ? (unsigned)(hi - lo) : 0u;
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const unsigned x = (unsigned)(base + 32 * kb + 8 * (r >> 2) + (r & 3));
+      s[kb][r] = x < width ? s[kb][r] : neg_inf();
+    }
 }
 
 // Key positions [lo, hi) that any query position in [p0, p1) may see (p1 > p0).
@@ -291,7 +321,7 @@ struct VtStager {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<void*>(ubase), (short)0, uniform((int)((uint32_t)v * row_stride)),
         0x00020000);
-    if (active) {
+    if (ITEMS >= 256 || active) {  // branch-free when every thread stages (head_dim 128)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         r[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -413,7 +443,7 @@ struct Mma<__bf16, D> {
   __device__ static float pack_p(const f32x16& p, PPack& pk) {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     typedef __attribute__((ext_vector_type(2))) float f32x2;
-    float sum = 0.0f;
+    float sum = p[0] + p[1];  // (a 0.0f start would cost an add: x + 0 is not x for -0)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       i32x4 w;
@@ -421,7 +451,7 @@ struct Mma<__bf16, D> {
       for (int i = 0; i < 4; ++i) {
         const f32x2 x = {p[8 * h + 2 * i], p[8 * h + 2 * i + 1]};
         w[i] = __builtin_bit_cast(int, __builtin_convertvector(x, bf16x2));
-        sum += x[0] + x[1];
+        if (h + i > 0) sum += x[0] + x[1];
       }
       pk.b[h] = __builtin_bit_cast(bf16x8, w);
     }

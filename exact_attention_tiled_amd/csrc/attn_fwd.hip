@@ -55,16 +55,7 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack 
                                              bool need_mask, int pq, int kpos0, const SeqGeom& g,
                                              int mode, int window, float c2, float& m_run,
                                              float& l_run, f32x16 (&o)[D / 32], int lane) {
-  const int hg = lane >> 5;
-  if (need_mask) {
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = pair_allowed(pq, kpos0 + 32 * kb + key_of_reg(r, hg), g, mode, window);
-        s[kb][r] = ok ? s[kb][r] : neg_inf();
-      }
-  }
+  if (need_mask) mask_blocks<NK>(s, pq, kpos0, g, mode, window, lane);
   float mx = neg_inf();
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb)
@@ -343,16 +334,7 @@ __device__ __forceinline__ float stage_max(f32x16 (&s)[2], bool need_mask, int p
                                            const SeqGeom& g, int mode, int window, float c2,
                                            float& m_run, float& l_run, f32x16 (&o)[D / 32],
                                            int lane) {
-  const int hg = lane >> 5;
-  if (need_mask) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = pair_allowed(pq, kpos0 + 32 * kb + key_of_reg(r, hg), g, mode, window);
-        s[kb][r] = ok ? s[kb][r] : neg_inf();
-      }
-  }
+  if (need_mask) mask_blocks<2>(s, pq, kpos0, g, mode, window, lane);
   float mx = neg_inf();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -386,8 +368,12 @@ __device__ __forceinline__ float stage_exp(f32x16 (&s)[2], typename Mma<__bf16, 
 
 // S_new = K_tile Q^T for both 32-key blocks, with the exponentials of the previous stage
 // (s_old -> pk) interleaved: per MFMA one operand read (PF ahead) and ~7 VALU instructions.
-template <int D>
-__device__ __forceinline__ float qk_with_exp(f32x16 (&sn)[2], const char* kt,
+// `issue` requests the next stage's K and V; its 8 buffer loads are spread over the first
+// 8 MFMAs. Issuing them in a burst before the contraction stalled the wave for ~400 cycles
+// per stage while the CU's memory pipeline accepted them (measured with per-phase cycle
+// stamps); behind the MFMAs that wait overlaps matrix work.
+template <int D, typename Issue>
+__device__ __forceinline__ float qk_with_exp(const Issue& issue, f32x16 (&sn)[2], const char* kt,
                                              const bf16x8 (&qr)[D / 16],
                                              const typename Mma<__bf16, D>::Offsets& of,
                                              f32x16 (&so)[2],
@@ -399,6 +385,7 @@ __device__ __forceinline__ float qk_with_exp(f32x16 (&sn)[2], const char* kt,
 #pragma unroll
   for (int i = 0; i < PF; ++i)
     a[i] = *reinterpret_cast<const bf16x8*>(kt + (i & 1) * 32 * ROWB + of.k[i >> 1]);
+  issue();
   sn[0] = f32x16{};
   sn[1] = f32x16{};
 #pragma unroll
@@ -415,6 +402,7 @@ __device__ __forceinline__ float qk_with_exp(f32x16 (&sn)[2], const char* kt,
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     if (i + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
   }
@@ -454,15 +442,22 @@ __device__ __forceinline__ void prefill_steady(const PipeCtx<D>& c, PipeRun<D>& 
   typedef Mma<__bf16, D> M;
   constexpr int BN = FWD_BN;
   const int kcur = c.kstart + j * BN;
-  if (j + 1 < c.nst)
+  // K_{j+1} (DMA) and V_j (registers). In the last iteration the K request covers no valid
+  // row: the descriptor's range check turns it into zero writes to a buffer nothing reads.
+  auto issue = [&]() {
     c.dma.issue(c.kg + (size_t)(kcur + BN) * c.rstride, c.g.len_k - kcur - BN, c.rstride,
                 kbuf[B ^ 1]);
-  c.vst.issue(c.vg + (size_t)kcur * c.rstride, c.g.len_k - kcur, c.rstride);
+    c.vst.issue(c.vg + (size_t)kcur * c.rstride, c.g.len_k - kcur, c.rstride);
+  };
   const float base = stage_max<D>(so, r.mask_prev, c.pq, kcur - BN, c.g, c.p.mode, c.p.window,
                                   c.p.c2, r.m_run, r.l_run, r.o, c.lane);
   typename M::PPack pk[2];
-  r.l_run += qk_with_exp<D>(sn, kbuf[B], c.qr, c.of, so, pk, c.p.c2, base);
+  // The two workgroups sharing a CU alternate: a wave in its contractions takes issue
+  // priority, so the co-resident wave's softmax and staging fill the MFMA shadow.
+  __builtin_amdgcn_s_setprio(1);
+  r.l_run += qk_with_exp<D>(issue, sn, kbuf[B], c.qr, c.of, so, pk, c.p.c2, base);
   M::pv2(r.o, pk, vbuf[B ^ 1], c.of);
+  __builtin_amdgcn_s_setprio(0);
   r.mask_prev = block_class(c.wp0, c.wp1, kcur, kcur + BN, c.g, c.p.mode, c.p.window) != 2;
   wait_vmem();
   c.vst.write(vbuf[B]);
