@@ -567,23 +567,37 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
   const float lt = sum_halves(r.l_run);
   const bool nonempty = lt > 0.0f;
   const float inv = nonempty ? 1.0f / lt : 0.0f;
-  if (qvalid) {
-    __bf16* orow = static_cast<__bf16*>(p.out) + ((size_t)(g.q_start + pq) * p.hq + h) * D;
-    const int hg = lane >> 5;
+  // O goes through LDS so that every store instruction writes whole 256-byte rows: in the
+  // accumulator layout a lane holds 8-byte pieces of one row, and storing those directly
+  // costs 32 partial-row writes per instruction. The K buffers are free here (the last K
+  // read preceded the last barrier; other waves may still read V^T), 8 KB per wave.
+  {
+    char* ot = (wave < 2 ? kbuf[0] : kbuf[1]) + (wave & 1) * 32 * ROWB;
+    const int i = lane & 31, hg = lane >> 5;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int d = db * 32 + 8 * a + 4 * hg;
-        M::store4(orow + d, nonempty ? r.o[db][4 * a] * inv : 0.0f,
-                  nonempty ? r.o[db][4 * a + 1] * inv : 0.0f,
-                  nonempty ? r.o[db][4 * a + 2] * inv : 0.0f,
-                  nonempty ? r.o[db][4 * a + 3] * inv : 0.0f);
+        // head-dim 32 db + 8 a + 4 hg + 0..3: 8 bytes in 16-byte chunk 4 db + a of row i
+        M::store4(reinterpret_cast<__bf16*>(ot + i * ROWB + (swz_chunk<ROWB>(i, 4 * db + a) << 4) + 8 * hg),
+                  nonempty ? r.o[db][4 * a] * inv : 0.0f, nonempty ? r.o[db][4 * a + 1] * inv : 0.0f,
+                  nonempty ? r.o[db][4 * a + 2] * inv : 0.0f, nonempty ? r.o[db][4 * a + 3] * inv : 0.0f);
       }
-    if (hg == 0)
-      p.lse[(size_t)h * p.total_q + g.q_start + pq] =
-          nonempty ? (r.m_run + fast_log2(lt)) * LN2 : neg_inf();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int CPR = ROWB / 16, RPI = 64 / CPR;  // 16-byte chunks per row, rows per instruction
+    const int c = lane % CPR;
+    const size_t rstep = (size_t)p.hq * D;
+    __bf16* obase = static_cast<__bf16*>(p.out) + ((size_t)(g.q_start + wp0) * p.hq + h) * D;
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int row = k * RPI + lane / CPR;
+      const i32x4 x = *reinterpret_cast<const i32x4*>(ot + row * ROWB + (swz_chunk<ROWB>(row, c) << 4));
+      if (wp0 + row < wp1) *reinterpret_cast<i32x4*>(obase + row * rstep + 8 * c) = x;
+    }
   }
+  if (qvalid && lane < 32)
+    p.lse[(size_t)h * p.total_q + g.q_start + pq] =
+        nonempty ? (r.m_run + fast_log2(lt)) * LN2 : neg_inf();
 }
 
 // Running state of one split-K wave: one block of 32 query rows over KBW consecutive
