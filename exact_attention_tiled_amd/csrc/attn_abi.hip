@@ -40,10 +40,41 @@ int validate_common(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t 
   return ATTN_OK;
 }
 
+std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_device_cu[64];  // compute units per device (0 unknown)
+
+// Checks that the current device is gfx950 (once per device) and reports its CU count.
+int check_device(int* num_cu = nullptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_UNSUPPORTED_DEVICE;
+  if (dev < 0 || dev >= 64) return ATTN_ERR_UNSUPPORTED_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_UNSUPPORTED_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_cu[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  if (num_cu) *num_cu = g_device_cu[dev].load(std::memory_order_relaxed);
+  return state == 1 ? ATTN_OK : ATTN_ERR_UNSUPPORTED_DEVICE;
+}
+
+// CU count used for planning: the current device's when it is a gfx950 (so the sizes a
+// caller queries match the launch on that device), else MI355X's 256.
+int planning_cu_count() {
+  int n = 0;
+  if (check_device(&n) != ATTN_OK || n <= 0) n = 256;
+  return n;
+}
+
 // Path choice. Split-K when the query rows of one K/V head fit one wave's two 32-row
 // blocks and the key range is long enough to be worth splitting; prefill otherwise.
+// num_cu sizes the split-K grid: the path is bound by HBM reads, and one CU keeps only so
+// many bytes in flight, so every CU must stream (one workgroup per CU fits in LDS).
 int make_plan(int32_t num_seqs, int32_t total_q, int32_t max_q, int32_t max_k, int32_t hq,
-              int32_t hkv, int32_t d, int32_t dtype, int32_t path, int32_t num_splits, Plan* plan) {
+              int32_t hkv, int32_t d, int32_t dtype, int32_t path, int32_t num_splits,
+              int num_cu, Plan* plan) {
   const int group = hq / hkv;
   const long rows = (long)group * max_q;
   // Two 128-key fp32 stages of head_dim 128 exceed the 160 KiB of LDS.
@@ -61,9 +92,21 @@ int make_plan(int32_t num_seqs, int32_t total_q, int32_t max_q, int32_t max_k, i
   const long max_blocks = std::max<long>(1, (max_k + stage - 1) / stage);
   long nsb = num_splits;
   if (nsb == 0) {
-    // Aim for about two workgroups per CU over the whole grid, at least 4 stages each.
+    // Fill every CU with as little imbalance as possible: among 1..4 times the smallest
+    // count that covers all CUs, the split count whose last round of workgroups is the
+    // fullest (ties: fewer splits, i.e. fewer partials to combine). At least 4 stages each.
     const long units = std::max<long>(1, (long)num_seqs * hkv);
-    nsb = (512 + units - 1) / units;
+    const long cus = std::max(1, num_cu);
+    const long base = std::max<long>(1, (cus + units - 1) / units);
+    double best = -1.0;
+    for (long c = base; c <= 4 * base; ++c) {
+      const long wgs = units * c, rounds = (wgs + cus - 1) / cus;
+      const double eff = (double)wgs / (double)(rounds * cus);
+      if (eff > best + 1e-9) {
+        best = eff;
+        nsb = c;
+      }
+    }
     nsb = std::min<long>(nsb, std::max<long>(1, (max_k + 4 * stage - 1) / (4 * stage)));
   }
   nsb = std::max<long>(1, std::min<long>(nsb, max_blocks));
@@ -76,22 +119,6 @@ int make_plan(int32_t num_seqs, int32_t total_q, int32_t max_q, int32_t max_k, i
   plan->workspace = attn::splitk_workspace_bytes(
       (int)nsb * attn::splitk_partials_per_chunk((int)rows), total_q, hq, d);
   return ATTN_OK;
-}
-
-std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, 2 other
-
-int check_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_UNSUPPORTED_DEVICE;
-  if (dev < 0 || dev >= 64) return ATTN_ERR_UNSUPPORTED_DEVICE;
-  int state = g_device_ok[dev].load(std::memory_order_relaxed);
-  if (state == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_UNSUPPORTED_DEVICE;
-    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    g_device_ok[dev].store(state, std::memory_order_relaxed);
-  }
-  return state == 1 ? ATTN_OK : ATTN_ERR_UNSUPPORTED_DEVICE;
 }
 
 FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q,
@@ -154,7 +181,8 @@ size_t attn_fwd_ex_workspace_size(int32_t num_seqs, int32_t total_q, int32_t tot
                       window) != ATTN_OK)
     return 0;
   Plan plan;
-  if (make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits, &plan) != ATTN_OK)
+  if (make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
+                planning_cu_count(), &plan) != ATTN_OK)
     return 0;
   return plan.workspace;
 }
@@ -176,7 +204,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_q
   if (rc != ATTN_OK) return rc;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   Plan plan;
-  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits, &plan);
+  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
+                 planning_cu_count(), &plan);
   if (rc != ATTN_OK) return rc;
   if (num_seqs == 0 || total_q == 0) return ATTN_OK;
   if (!cu_q || !cu_k || !out || !lse || !q) return ATTN_ERR_NULL_PTR;
@@ -271,7 +300,8 @@ int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32
                            window);
   if (rc != ATTN_OK) return rc;
   Plan plan;
-  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits, &plan);
+  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
+                 planning_cu_count(), &plan);
   if (rc != ATTN_OK) return rc;
   if (!buf || len == 0) return ATTN_ERR_NULL_PTR;
   const char* dt = dtype == ATTN_BF16 ? "bf16" : "f32";

@@ -662,9 +662,9 @@ struct SplitkWave {
 // G * len_q (query head, query position) pairs of the group, so every K/V byte is read
 // once for the whole group. With NRB row blocks of 32, wave w owns row block w % NRB and
 // KBW = NRB consecutive 32-key blocks of every 128-key stage (the waves sharing a row
-// block split the stage's keys); each wave keeps its own running state and writes its own
-// partial (O_e normalised, LSE_e), e = chunk * (4 / NRB) + w / NRB. The combine kernel
-// merges the partials of each row.
+// block split the stage's keys); each wave keeps its own running state, the waves of a row
+// block merge their states at the end, and the chunk writes one partial (O_e normalised,
+// LSE_e), e = chunk. The combine kernel merges the partials of each row.
 // ---------------------------------------------------------------------------------------
 template <typename T, int D, int NRB>
 __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
@@ -745,13 +745,69 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
     }
   }
 
-  // Partial e of this wave: normalised O_e (fp32) and LSE_e; empty -> O_e = 0, LSE_e = -inf.
-  const int e = sigma * KW + kwi;
+  // The KW waves of a row block hold partial softmax states (O unnormalised, offset m in
+  // log2 units, denominator l) over disjoint keys of the chunk. They are merged here through
+  // LDS (the stage buffers are free after the last barrier), so the chunk writes ONE partial
+  // per row: M = max m_w, l = sum l_w 2^(m_w - M), O = sum O_w 2^(m_w - M). Waves that saw
+  // no key (m_w = -inf) weigh 0.
+  constexpr int NO = D / 32 * 16;  // O values per lane
+  float lt = sum_halves(st.l_run);
+  float mt = st.m_run;
+  if constexpr (KW > 1) {
+    float* red = reinterpret_cast<float*>(buf0);  // per (row block, wave > 0): O, m, l
+    constexpr int SLOT = (NO + 2) * 64;
+    static_assert(NRB * (KW - 1) * SLOT * 4 <= 2 * TILE, "merge area must fit one stage buffer");
+    if (kwi > 0) {
+      float* sl = red + (rb * (KW - 1) + kwi - 1) * SLOT;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sl[(db * 16 + i) * 64 + lane] = st.o[db][i];
+      sl[NO * 64 + lane] = mt;
+      sl[(NO + 1) * 64 + lane] = lt;
+    }
+    __syncthreads();
+    if (kwi == 0) {
+      float mw[KW], lw[KW];
+      mw[0] = mt;
+      lw[0] = lt;
+#pragma unroll
+      for (int w = 1; w < KW; ++w) {
+        const float* sl = red + (rb * (KW - 1) + w - 1) * SLOT;
+        mw[w] = sl[NO * 64 + lane];
+        lw[w] = sl[(NO + 1) * 64 + lane];
+      }
+      float mm = mw[0];
+#pragma unroll
+      for (int w = 1; w < KW; ++w) mm = fmaxf(mm, mw[w]);
+      float sc[KW];
+      lt = 0.0f;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) {
+        sc[w] = mw[w] == neg_inf() ? 0.0f : fast_exp2(mw[w] - mm);
+        lt += lw[w] * sc[w];
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float acc = st.o[db][i] * sc[0];
+#pragma unroll
+          for (int w = 1; w < KW; ++w)
+            acc += red[(rb * (KW - 1) + w - 1) * SLOT + (db * 16 + i) * 64 + lane] * sc[w];
+          st.o[db][i] = acc;
+        }
+      mt = mm;
+    }
+  }
+
+  // The row block's partial for this chunk: normalised O_e (fp32) and LSE_e; empty -> O_e = 0,
+  // LSE_e = -inf.
+  const int e = sigma;
   const int hg = lane >> 5;
-  const float lt = sum_halves(st.l_run);
   const bool nonempty = lt > 0.0f;
   const float inv = nonempty ? 1.0f / lt : 0.0f;
-  if (rvalid) {
+  if (kwi == 0 && rvalid) {
     const int t = g.q_start + pq;
     const int h = kvh * G + r % G;
     float* dst = p.part_o + (((size_t)e * p.total_q + t) * p.hq + h) * D;
@@ -766,7 +822,7 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
       }
     if (hg == 0)
       p.part_lse[((size_t)e * p.hq + h) * p.total_q + t] =
-          nonempty ? (st.m_run + fast_log2(lt)) * LN2 : neg_inf();
+          nonempty ? (mt + fast_log2(lt)) * LN2 : neg_inf();
   }
 }
 
@@ -903,7 +959,7 @@ hipError_t launch_fwd_prefill(const FwdArgs& a, hipStream_t st) {
   return a.d == 64 ? prefill_typed<float, 64>(a, st) : prefill_typed<float, 128>(a, st);
 }
 
-int splitk_partials_per_chunk(int rows) { return rows <= 32 ? 4 : 2; }
+int splitk_partials_per_chunk(int) { return 1; }
 
 size_t splitk_workspace_bytes(int nsplit_eff, int total_q, int hq, int d) {
   const size_t o = (size_t)nsplit_eff * total_q * hq * d * sizeof(float);

@@ -45,8 +45,7 @@ bool equal_lengths(const FwdArgs& a);
 int fwd_prefill_grid(const FwdArgs& a);
 hipError_t launch_fwd_prefill(const FwdArgs& a, hipStream_t stream);
 
-// Partials per key chunk of the split-K path: one per wave sharing a row block (four for
-// at most 32 rows per K/V head, two for 33..64).
+// Partials per key chunk of the split-K path (the waves of a workgroup merge theirs).
 int splitk_partials_per_chunk(int rows);
 size_t splitk_workspace_bytes(int nsplit_eff, int total_q, int hq, int d);
 hipError_t launch_fwd_splitk(const FwdArgs& a, int blocks_per_kvh, int chunk, void* workspace,
