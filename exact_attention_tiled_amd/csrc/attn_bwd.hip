@@ -244,14 +244,23 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa8, ka8, sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da8, va8, dpacc, 0, 0, 0);
       }
-      // P and dS; register r holds query row 32 qh + key_of_reg(r, g) of the tile.
+      // P and dS; register r holds query row 32 qh + key_of_reg(r, g) of the tile. Registers
+      // 4a..4a+3 hold 4 consecutive rows, so LSE2 and D arrive in 16-byte reads. The weight
+      // is computed for every element and then selected: a conditional exponential became
+      // one divergent branch per element, each serialising its LDS reads.
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        l4[a] = *reinterpret_cast<const f32x4*>(lse2s + 32 * qh + 8 * a + 4 * hg);
+        d4[a] = *reinterpret_cast<const f32x4*>(dvs + 32 * qh + 8 * a + 4 * hg);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 32 * qh + key_of_reg(r, hg);
         const bool ok = qbase + (unsigned)(8 * (r >> 2) + (r & 3)) < qwidth;
-        const float pv = ok ? fast_exp2(fmaf(sacc[r], p.c, -lse2s[row])) : 0.0f;
+        const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[r >> 2][r & 3]));
+        const float pv = ok ? e : 0.0f;
         sacc[r] = pv;
-        dpacc[r] = pv * (dpacc[r] - dvs[row]);
+        dpacc[r] = pv * (dpacc[r] - d4[r >> 2][r & 3]);
       }
       M::pack_p(sacc, pp[0]);
       M::pack_p(dpacc, pd[0]);
@@ -379,7 +388,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const bool ok = kbase + (unsigned)(32 * kb + 8 * (r >> 2) + (r & 3)) < kwidth;
-        const float pv = ok ? fast_exp2(fmaf(sacc[r], p.c, -l2)) : 0.0f;
+        const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));  // computed, then selected
+        const float pv = ok ? e : 0.0f;
         sacc[r] = pv * (dpacc[r] - dvl);
       }
       typename M::PPack pk;
