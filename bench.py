@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|ragged|decode16|
                     decode1|decode4|train|train_w1024] [--no-secondary] [--cpu-seconds S]
+    python bench.py --sweep [--steps K] [--warmup W]    (sequence-length scaling and memory)
 
 Headline (one JSON line on stdout): the dense bf16 causal forward workload (B=4, Hq=Hkv=16,
 N=2048, d=128, causal top-left), reported as causal-adjusted TFLOP/s: 4 * d * (allowed
@@ -223,7 +224,7 @@ def bench_forward(w, steps, warmup, validate=True):
     return {"wall_s": wall, "mean_ms": mean_ms, "ms": ms, "plan": plan, "validated": valid}
 
 
-def bench_train(w, steps, warmup):
+def bench_train(w, steps, warmup, validate=True):
     import torch
     import exact_attention_tiled_amd as eat
     dev = torch.device("cuda:0")
@@ -252,8 +253,10 @@ def bench_train(w, steps, warmup):
 
     step()
     torch.cuda.synchronize()
-    if not validate_sample(w, out, lse, grads=(dq, dk, dv)):
+    if validate and not validate_sample(w, out, lse, grads=(dq, dk, dv)):
         raise SystemExit(f"validation against the oracle failed for {w.name}; not timing it")
+    # Peak memory of the timed calls only (validation makes float64 copies).
+    torch.cuda.reset_peak_memory_stats()
     wall, mean_ms, ms = time_steps(step, steps, warmup)
     _, mean_f, ms_f = time_steps(fwd, steps, 2)
     _, mean_b, ms_b = time_steps(bwd, steps, 2)
@@ -298,6 +301,70 @@ def cpu_baseline(w, target_s: float):
 
 
 # ----------------------------------------------------------------------------------------
+# Sequence-length scaling and memory ("Attention Algorithm Error and Complexity Tests",
+# fifth and sixth sections: pair work, fitted exponents, saved state and workspace).
+# ----------------------------------------------------------------------------------------
+
+def fit_power(ns, ts):
+    """Least-squares fit of t = a * N^k on log-log axes; returns (k, a, max relative residual)."""
+    x = np.log(np.asarray(ns, dtype=np.float64))
+    y = np.log(np.asarray(ts, dtype=np.float64))
+    k, loga = np.polyfit(x, y, 1)
+    resid = np.exp(y - (k * x + loga)) - 1.0
+    return float(k), float(np.exp(loga)), float(np.abs(resid).max())
+
+
+def sweep(steps: int, warmup: int, validate_max_n: int = 4096):
+    """Training step (forward and backward timed separately) of one sequence of N tokens with
+    Hq=32, Hkv=8, d=128, bf16, causal top-left, without and with a 1024-key window, for N from
+    1k to 32k; everything else fixed. Outputs are checked against the oracle for N <= 4096."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    ns = [1024, 2048, 4096, 8192, 16384, 32768]
+    rows = []
+    for window in (0, 1024):
+        for n in ns:
+            w = wl.train_bf16(window=window, seqlen=n, batch=1)
+            pairs = allowed_pairs(w)
+            torch.cuda.empty_cache()
+            r = bench_train(w, steps, warmup, validate=n <= validate_max_n)
+            ws_bwd = eat.attn_bwd_workspace_size(
+                torch.empty((w.total_q, w.hq, w.d), dtype=torch.bfloat16, device="meta"),
+                torch.empty((w.total_k, w.hkv, w.d), dtype=torch.bfloat16, device="meta"),
+                torch.empty((w.num_seqs + 1,), dtype=torch.int32, device="meta"),
+                w.max_seqlen_q, w.max_seqlen_k, w.mask_mode, w.window)
+            el = 2
+            io_bytes = el * (w.q.size * 2 + w.k.size + w.v.size) + 4 * w.hq * w.total_q
+            rows.append({
+                "n": n, "window": window, "allowed_pairs": pairs,
+                "fwd_ms": float(np.median(r["ms_fwd"])), "bwd_ms": float(np.median(r["ms_bwd"])),
+                "fwd_tflops": 4.0 * w.d * pairs / (np.median(r["ms_fwd"]) * 1e-3) / 1e12,
+                "bwd_tflops": 10.0 * w.d * pairs / (np.median(r["ms_bwd"]) * 1e-3) / 1e12,
+                "fwd_io_bytes": io_bytes, "bwd_workspace_bytes": int(ws_bwd),
+                # q, k, v, out, lse, dout, dq, dk, dv and the backward workspace
+                "train_tensor_bytes": int(el * (w.q.size * 4 + w.k.size * 4) + 4 * w.hq * w.total_q
+                                          + ws_bwd),
+                "fwd_workspace_bytes": 0,
+                "torch_peak_allocated_bytes": int(torch.cuda.max_memory_allocated()),
+                "torch_peak_reserved_bytes": int(torch.cuda.max_memory_reserved()),
+                "validated": n <= validate_max_n})
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            del w
+    fits = {}
+    for window in (0, 1024):
+        sel = [r for r in rows if r["window"] == window]
+        for key in ("fwd_ms", "bwd_ms", "allowed_pairs", "torch_peak_allocated_bytes"):
+            k, a, res = fit_power([r["n"] for r in sel], [r[key] for r in sel])
+            fits[f"window{window}_{key}"] = {"exponent": k, "coefficient": a, "max_rel_residual": res}
+        # the window's pair count is linear only once N >> window: fit the upper half too
+        hi = [r for r in sel if r["n"] >= 8192]
+        k, a, res = fit_power([r["n"] for r in hi], [r["fwd_ms"] for r in hi])
+        fits[f"window{window}_fwd_ms_n_ge_8192"] = {"exponent": k, "coefficient": a, "max_rel_residual": res}
+    print(json.dumps({"sweep": "sequence-length scaling, B=1 Hq=32 Hkv=8 d=128 bf16 causal top-left",
+                      "steps": steps, "warmup": warmup, "rows": rows, "fits": fits}))
+
+
+# ----------------------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -310,6 +377,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="sequence-length scaling and memory sweep (prints its own JSON)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -331,6 +400,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": args.steps}))
+        return
+
+    if args.sweep:
+        sweep(args.steps, args.warmup)
         return
 
     w = make_workload(args.workload)
