@@ -94,7 +94,9 @@ enum attn_path { ATTN_PATH_AUTO = 0, ATTN_PATH_PREFILL = 1, ATTN_PATH_SPLITK = 2
  *   scale            finite multiplier of q.k (usually 1/sqrt(head_dim))
  *   mask_mode        attn_mask_mode; window > 0 needs a causal mode, window <= 0 = none
  *   workspace        device scratch of at least attn_fwd_workspace_size(...) bytes (may be
- *                    NULL when that size is 0); its contents need no initialisation
+ *                    NULL when that size is 0); its contents need no initialisation. The
+ *                    split-K plan sizes its grid by the CU count of the current device, so
+ *                    query the size with the device current that will run the call.
  */
 int attn_fwd(const void* q, const void* k, const void* v,
              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
