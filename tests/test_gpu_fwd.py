@@ -115,16 +115,17 @@ def test_splitk_decode_shapes(dtype, mode, window, nq, group):
     (300, 450, 2, 0), (300, 450, 1, 0), (450, 300, 2, 0), (450, 300, 1, 0), (257, 257, 0, 0),
     (384, 384, 1, 100), (200, 600, 2, 129), (1, 1, 1, 0)])
 @pytest.mark.parametrize("hq,hkv", [(6, 2), (8, 8), (12, 3)])
-def test_equal_length_batches(lq, lk, mode, window, hq, hkv):
+@pytest.mark.parametrize("d", [64, 128])
+def test_equal_length_batches(lq, lk, mode, window, hq, hkv, d):
     """Every sequence of the pack has the same lengths (ragged tails inside the last tile),
     head counts that are and are not multiples of 8; against the oracle, and bitwise equal
     to the same sequences preceded by a one-token sequence (which forces the slot order)."""
     import exact_attention_tiled_amd as eat
     import torch
     nseq = 3
-    w = wl.random_workload((14, lq, lk, mode, hq), [lq] * nseq, [lk] * nseq, hq, hkv, 64,
+    w = wl.random_workload((14, lq, lk, mode, hq), [lq] * nseq, [lk] * nseq, hq, hkv, d,
                            "bf16", mode, window, name="equal", v_offsets=True)
-    print(f"equal-length lq={lq} lk={lk} mode={mode} window={window} hq={hq} hkv={hkv}",
+    print(f"equal-length lq={lq} lk={lk} mode={mode} window={window} hq={hq} hkv={hkv} d={d}",
           flush=True)
     t = to_device(w)
     plan = eat.attn_describe_plan(t["q"], t["k"], t["cu_q"], w.max_seqlen_q, w.max_seqlen_k,
