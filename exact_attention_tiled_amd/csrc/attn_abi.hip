@@ -72,9 +72,9 @@ int planning_cu_count() {
 // blocks and the key range is long enough to be worth splitting; prefill otherwise.
 // num_cu sizes the split-K grid: the path is bound by HBM reads, and one CU keeps only so
 // many bytes in flight, so every CU must stream (one workgroup per CU fits in LDS).
-int make_plan(int32_t num_seqs, int32_t total_q, int32_t max_q, int32_t max_k, int32_t hq,
-              int32_t hkv, int32_t d, int32_t dtype, int32_t path, int32_t num_splits,
-              int num_cu, Plan* plan) {
+int make_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
+              int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype, int32_t path,
+              int32_t num_splits, int num_cu, Plan* plan) {
   const int group = hq / hkv;
   const long rows = (long)group * max_q;
   // Two 128-key fp32 stages of head_dim 128 exceed the 160 KiB of LDS.
@@ -86,7 +86,17 @@ int make_plan(int32_t num_seqs, int32_t total_q, int32_t max_q, int32_t max_k, i
   plan->nsb = 0;
   plan->chunk = 0;
   plan->workspace = 0;
-  if (path == ATTN_PATH_PREFILL) return ATTN_OK;
+  if (path == ATTN_PATH_PREFILL) {
+    // Batches of unequal lengths sort their tiles by cost (one int32 per tile slot).
+    attn::FwdArgs a{};
+    a.num_seqs = num_seqs;
+    a.total_q = total_q;
+    a.total_k = total_k;
+    a.max_q = max_q;
+    a.max_k = max_k;
+    plan->workspace = attn::fwd_prefill_workspace_bytes(a);
+    return ATTN_OK;
+  }
   if (!splitk_ok) return ATTN_ERR_BAD_PLAN;
   const int stage = attn::SPLITK_STAGE;
   const long max_blocks = std::max<long>(1, (max_k + stage - 1) / stage);
@@ -181,7 +191,7 @@ size_t attn_fwd_ex_workspace_size(int32_t num_seqs, int32_t total_q, int32_t tot
                       window) != ATTN_OK)
     return 0;
   Plan plan;
-  if (make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
+  if (make_plan(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
                 planning_cu_count(), &plan) != ATTN_OK)
     return 0;
   return plan.workspace;
@@ -204,7 +214,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_q
   if (rc != ATTN_OK) return rc;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   Plan plan;
-  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
+  rc = make_plan(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
                  planning_cu_count(), &plan);
   if (rc != ATTN_OK) return rc;
   if (num_seqs == 0 || total_q == 0) return ATTN_OK;
@@ -218,7 +228,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_q
                               hkv, d, dtype, scale, mode, window, out, lse);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = plan.path == ATTN_PATH_PREFILL
-                     ? attn::launch_fwd_prefill(a, st)
+                     ? attn::launch_fwd_prefill(a, workspace, st)
                      : attn::launch_fwd_splitk(a, plan.nsb, plan.chunk, workspace, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
 }
@@ -300,7 +310,7 @@ int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32
                            window);
   if (rc != ATTN_OK) return rc;
   Plan plan;
-  rc = make_plan(num_seqs, total_q, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
+  rc = make_plan(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, path, num_splits,
                  planning_cu_count(), &plan);
   if (rc != ATTN_OK) return rc;
   if (!buf || len == 0) return ATTN_ERR_NULL_PTR;
@@ -309,11 +319,11 @@ int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32
     FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, num_seqs, total_q, total_k,
                           max_q, max_k, hq, hkv, d, dtype, 1.0f, mode, window, nullptr, nullptr);
     std::snprintf(buf, len,
-                  "path=prefill dtype=%s d=%d tile=%dx%d waves=4 order=%s grid=%d workspace=0 "
+                  "path=prefill dtype=%s d=%d tile=%dx%d waves=4 order=%s grid=%d workspace=%zu "
                   "version=%d",
                   dt, d, attn::FWD_BM, attn::FWD_BN,
-                  attn::equal_lengths(a) ? "largest_first" : "slots", attn::fwd_prefill_grid(a),
-                  ATTN_VERSION);
+                  attn::equal_lengths(a) ? "largest_first" : "cost_sorted",
+                  attn::fwd_prefill_grid(a), plan.workspace, ATTN_VERSION);
   } else {
     std::snprintf(buf, len,
                   "path=splitk dtype=%s d=%d stage=%d rows_per_kvhead<=%d blocks_per_kvhead=%d "

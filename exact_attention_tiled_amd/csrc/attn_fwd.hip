@@ -33,6 +33,7 @@ struct FwdParams {
   int nslots, nlogical;
   int uni_ntiles, npairs;
   int uni_lq, uni_lk;  // equal-length batch: every sequence's query / key length
+  const int32_t* order;  // other batches: slots sorted by cost (prefill_order_kernel), -1 pads
   // split-K
   float* part_o;
   float* part_lse;
@@ -119,10 +120,21 @@ __device__ __forceinline__ bool prefill_tile(const FwdParams& p, int& h, int& s,
     tile = p.uni_ntiles - 1 - rank;  // latest (heaviest under causal masks) tiles first
     return tile < ntiles;
   }
-  const int w = xcd_logical_block(blockIdx.x, p.nlogical);
-  if (w < 0) return false;
-  h = w / p.nslots;
-  const int slot = w - h * p.nslots;
+  int slot;
+  if (p.order != nullptr) {
+    // Block b takes sorted slot b / Hq for query head b % Hq, K/V head fastest: with Hq a
+    // multiple of 8 the round-robin XCD assignment keeps each GQA group on one XCD.
+    const int b = blockIdx.x;
+    const int idx = b / p.hq, hp = b - idx * p.hq;
+    slot = p.order[idx];
+    if (slot < 0) return false;
+    h = (hp % p.hkv) * p.group + hp / p.hkv;
+  } else {
+    const int w = xcd_logical_block(blockIdx.x, p.nlogical);
+    if (w < 0) return false;
+    h = w / p.nslots;
+    slot = w - h * p.nslots;
+  }
   s = seq_of_slot<BM>(p.cu_q, p.num_seqs, slot);
   g = load_geom(p.cu_q, p.cu_k, s, p.mode);
   const int ntiles = (g.len_q + BM - 1) / BM;
@@ -894,6 +906,89 @@ __global__ void mask_probe_kernel(const int32_t* cu_q, const int32_t* cu_k, int 
 }
 
 // ---------------------------------------------------------------------------------------
+// Tile order of a prefill over sequences of different lengths. Every (sequence, query
+// tile) slot gets its cost - the number of 64-key stages its rows visit - and the slots
+// are sorted by cost, most first, with a counting sort in one workgroup (buckets beyond
+// ORDER_BUCKETS - 1 stages share the last one). The prefill then dispatches the heaviest
+// tiles first over all sequences (largest-first list scheduling), instead of in sequence
+// order, where the long tiles of the last sequences ran last and left a tail. Padding
+// slots (a sequence has fewer tiles than its slot range) are dropped; entries past the
+// valid count are -1. Ties are written in atomic order: tiles are independent, so the
+// order changes no result.
+// ---------------------------------------------------------------------------------------
+constexpr int ORDER_BUCKETS = 4096;
+constexpr int ORDER_THREADS = 1024;
+
+// (per lane: every lane of the sorting workgroup has its own slot)
+template <int BM>
+__device__ __forceinline__ int slot_cost(const int32_t* cu_q, const int32_t* cu_k, int num_seqs,
+                                         int mode, int window, int slot) {
+  int lo = 0, hi = num_seqs - 1;  // sequence of the slot: largest s with cu_q[s] / BM + s <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] / BM + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  const SeqGeom g = load_geom_lane(cu_q, cu_k, s, mode);
+  const int ntiles = (g.len_q + BM - 1) / BM;
+  const int j = slot - (g.q_start / BM + s);
+  if (j >= ntiles) return -1;
+  const int tile = ntiles - 1 - j;
+  const int p0 = tile * BM, p1 = min(p0 + BM, g.len_q);
+  int klo, khi;
+  visible_keys(p0, p1, g, mode, window, klo, khi);
+  const int kstart = (klo / FWD_BN) * FWD_BN;
+  const int nst = khi > klo ? (khi - kstart + FWD_BN - 1) / FWD_BN : 0;
+  return min(nst, ORDER_BUCKETS - 1);
+}
+
+template <int BM>
+__global__ __launch_bounds__(ORDER_THREADS) void prefill_order_kernel(
+    const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int nslots, int mode, int window,
+    int32_t* order) {
+  constexpr int PER = ORDER_BUCKETS / ORDER_THREADS;
+  __shared__ int hist[ORDER_BUCKETS];
+  __shared__ int part[ORDER_THREADS];
+  const int tid = threadIdx.x;
+  for (int b = tid; b < ORDER_BUCKETS; b += ORDER_THREADS) hist[b] = 0;
+  __syncthreads();
+  for (int slot = tid; slot < nslots; slot += ORDER_THREADS) {
+    const int c = slot_cost<BM>(cu_q, cu_k, num_seqs, mode, window, slot);
+    if (c >= 0) atomicAdd(&hist[c], 1);
+  }
+  __syncthreads();
+  // First position of each cost: the number of slots that cost more. Thread t owns the
+  // PER buckets ORDER_BUCKETS - 1 - PER t - i (descending); a scan over the threads' sums.
+  int local[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    local[i] = hist[ORDER_BUCKETS - 1 - PER * tid - i];
+    sum += local[i];
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < ORDER_THREADS; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    hist[ORDER_BUCKETS - 1 - PER * tid - i] = run;
+    run += local[i];
+  }
+  const int count = part[ORDER_THREADS - 1];
+  __syncthreads();
+  for (int slot = tid; slot < nslots; slot += ORDER_THREADS) {
+    const int c = slot_cost<BM>(cu_q, cu_k, num_seqs, mode, window, slot);
+    if (c >= 0) order[atomicAdd(&hist[c], 1)] = slot;
+  }
+  for (int i = count + tid; i < nslots; i += ORDER_THREADS) order[i] = -1;
+}
+
+// ---------------------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------------------
 static FwdParams make_params(const FwdArgs& a) {
@@ -931,12 +1026,17 @@ int fwd_prefill_grid(const FwdArgs& a) {
   const long ntiles = (a.max_q + FWD_BM - 1) / FWD_BM;
   if (equal_lengths(a)) return (int)(ntiles * a.num_seqs * a.hq);
   const long nslots = (long)a.total_q / FWD_BM + a.num_seqs;
-  const long nlogical = nslots * a.hq;
-  return (int)(((nlogical + 7) / 8) * 8);
+  return (int)(nslots * a.hq);
+}
+
+size_t fwd_prefill_workspace_bytes(const FwdArgs& a) {
+  if (equal_lengths(a)) return 0;
+  const size_t nslots = (size_t)a.total_q / FWD_BM + a.num_seqs;
+  return ((nslots * sizeof(int32_t) + 255) / 256) * 256;
 }
 
 template <typename T, int D>
-static hipError_t prefill_typed(const FwdArgs& a, hipStream_t st) {
+static hipError_t prefill_typed(const FwdArgs& a, void* ws, hipStream_t st) {
   FwdParams p = make_params(a);
   p.nslots = a.total_q / FWD_BM + a.num_seqs;
   p.nlogical = p.nslots * a.hq;
@@ -945,6 +1045,13 @@ static hipError_t prefill_typed(const FwdArgs& a, hipStream_t st) {
     p.npairs = a.num_seqs * a.hq;
     p.uni_lq = a.max_q;
     p.uni_lk = a.max_k;
+  } else {
+    p.order = static_cast<const int32_t*>(ws);
+    hipLaunchKernelGGL((prefill_order_kernel<FWD_BM>), dim3(1), dim3(ORDER_THREADS), 0, st,
+                       a.cu_q, a.cu_k, a.num_seqs, p.nslots, a.mode, a.window,
+                       static_cast<int32_t*>(ws));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   const int grid = fwd_prefill_grid(a);
   if constexpr (std::is_same<T, __bf16>::value)
@@ -954,9 +1061,10 @@ static hipError_t prefill_typed(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_prefill(const FwdArgs& a, hipStream_t st) {
-  if (a.dtype == 0) return a.d == 64 ? prefill_typed<__bf16, 64>(a, st) : prefill_typed<__bf16, 128>(a, st);
-  return a.d == 64 ? prefill_typed<float, 64>(a, st) : prefill_typed<float, 128>(a, st);
+hipError_t launch_fwd_prefill(const FwdArgs& a, void* ws, hipStream_t st) {
+  if (a.dtype == 0)
+    return a.d == 64 ? prefill_typed<__bf16, 64>(a, ws, st) : prefill_typed<__bf16, 128>(a, ws, st);
+  return a.d == 64 ? prefill_typed<float, 64>(a, ws, st) : prefill_typed<float, 128>(a, ws, st);
 }
 
 int splitk_partials_per_chunk(int) { return 1; }

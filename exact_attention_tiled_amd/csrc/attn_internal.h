@@ -43,7 +43,10 @@ constexpr int SPLITK_MAX_ROWS = 64;
 // orders its tiles heaviest first across all (sequence, head) pairs.
 bool equal_lengths(const FwdArgs& a);
 int fwd_prefill_grid(const FwdArgs& a);
-hipError_t launch_fwd_prefill(const FwdArgs& a, hipStream_t stream);
+// Other batches sort their tiles by cost first (a small kernel writing the order into the
+// workspace: one int32 per slot).
+size_t fwd_prefill_workspace_bytes(const FwdArgs& a);
+hipError_t launch_fwd_prefill(const FwdArgs& a, void* workspace, hipStream_t stream);
 
 // Partials per key chunk of the split-K path (the waves of a workgroup merge theirs).
 int splitk_partials_per_chunk(int rows);

@@ -95,8 +95,11 @@ enum attn_path { ATTN_PATH_AUTO = 0, ATTN_PATH_PREFILL = 1, ATTN_PATH_SPLITK = 2
  *   mask_mode        attn_mask_mode; window > 0 needs a causal mode, window <= 0 = none
  *   workspace        device scratch of at least attn_fwd_workspace_size(...) bytes (may be
  *                    NULL when that size is 0); its contents need no initialisation. The
- *                    split-K plan sizes its grid by the CU count of the current device, so
- *                    query the size with the device current that will run the call.
+ *                    split-K plan keeps its partial results there and sizes its grid by the
+ *                    CU count of the current device, so query the size with the device
+ *                    current that will run the call. A prefill over sequences of unequal
+ *                    lengths keeps its cost-sorted tile order there (4 bytes per query-tile
+ *                    slot: total_q / 128 + num_seqs slots); one of equal lengths needs none.
  */
 int attn_fwd(const void* q, const void* k, const void* v,
              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

@@ -119,7 +119,7 @@ def test_splitk_decode_shapes(dtype, mode, window, nq, group):
 def test_equal_length_batches(lq, lk, mode, window, hq, hkv, d):
     """Every sequence of the pack has the same lengths (ragged tails inside the last tile),
     head counts that are and are not multiples of 8; against the oracle, and bitwise equal
-    to the same sequences preceded by a one-token sequence (which forces the slot order)."""
+    to the same sequences preceded by a one-token sequence (which forces the cost-sorted order)."""
     import exact_attention_tiled_amd as eat
     import torch
     nseq = 3
@@ -143,7 +143,7 @@ def test_equal_length_batches(lq, lk, mode, window, hq, hkv, d):
     cu_k1 = torch.cat([t["cu_k"][:1], t["cu_k"] + 1])
     plan1 = eat.attn_describe_plan(q1, k1, cu_q1, w.max_seqlen_q, w.max_seqlen_k, w.mask_mode,
                                    w.window)
-    assert "order=slots" in plan1, plan1
+    assert "order=cost_sorted" in plan1, plan1
     out1, lse1 = eat.attn_fwd(q1, k1, v1, cu_q1, cu_k1, w.max_seqlen_q, w.max_seqlen_k, w.scale,
                               w.mask_mode, w.window, path=PREFILL)
     torch.cuda.synchronize()
