@@ -604,7 +604,10 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
     for (int k = 0; k < 32 / RPI; ++k) {
       const int row = k * RPI + lane / CPR;
       const i32x4 x = *reinterpret_cast<const i32x4*>(ot + row * ROWB + (swz_chunk<ROWB>(row, c) << 4));
-      if (wp0 + row < wp1) *reinterpret_cast<i32x4*>(obase + row * rstep + 8 * c) = x;
+      // Nontemporal: O is not read again by this call, and its lines would otherwise
+      // displace K/V lines that other tiles still read from L2.
+      if (wp0 + row < wp1)
+        __builtin_nontemporal_store(x, reinterpret_cast<i32x4*>(obase + row * rstep + 8 * c));
     }
   }
   if (qvalid && lane < 32)
@@ -722,7 +725,7 @@ __global__ __launch_bounds__(256, 1) void fwd_splitk_kernel(FwdParams p) {
   const uint32_t rstride = (uint32_t)(p.hkv * D * sizeof(T));
   const char* kb0 = static_cast<const char*>(p.k) + ((size_t)g.k_start * p.hkv + kvh) * D * sizeof(T);
   const char* vb0 = static_cast<const char*>(p.v) + ((size_t)g.k_start * p.hkv + kvh) * D * sizeof(T);
-  DmaStager<ROWB, BN, 4> dma;
+  DmaStager<ROWB, BN, 4, CPOL_NT> dma;  // every K/V byte is read once per call
   dma.init(wave, lane, rstride);
 
   // This wave's key blocks start at block kwi * KBW of each stage.
