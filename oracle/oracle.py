@@ -26,6 +26,12 @@ Readings taken where the pages are silent:
   * LSE of an all-masked row is -inf; LSE is the natural log-sum-exp of the scaled logits,
     stored [Hq, total_q].
   * GQA grouping is consecutive: query head h reads K/V head h // (Hq // Hkv).
+  * Dropout ("Attention Algorithm Error and Complexity Tests" page, first and fourth
+    sections; "Causal Mask and Ragged Sequence Layouts" page, sixth section: replay must
+    follow logical indices): inverted dropout on the normalised weights,
+    O = (P * keep / (1 - p)) V, with the LSE of the undropped softmax. The keep flag of
+    (sequence index, query head, in-sequence query position, in-sequence key position)
+    comes from Philox4x32-10 (dropout_keep below); p is rounded to a multiple of 1/256.
 
 All arithmetic is float64 (numpy). Inputs may be any float dtype; they are upcast exactly.
 Every function is pinned by tests in tests/test_oracle_*.py (closed forms, invariants,
@@ -142,8 +148,13 @@ def attention_explicit(q, k, v, mask, scale):
     return o, lse
 
 
-def attention(q, k, v, cu_q, cu_k, scale, mask_mode, window=0, seqs=None, heads=None):
+def attention(q, k, v, cu_q, cu_k, scale, mask_mode, window=0, seqs=None, heads=None,
+              dropout_p=0.0, seed=0):
     """Varlen GQA attention: O [Tq, Hq, d], LSE [Hq, Tq] in float64.
+
+    With dropout_p > 0 the weights that reach V are P * keep / (1 - t/256) with the keep
+    flags of ``dropout_keep`` (t = ``dropout_threshold(dropout_p)``); the LSE stays that of
+    the undropped softmax.
 
     The mask of every query row is built from sequence ids and in-sequence positions. A
     pair can only be allowed inside one sequence, so each sequence's rows are evaluated
@@ -172,6 +183,7 @@ def attention(q, k, v, cu_q, cu_k, scale, mask_mode, window=0, seqs=None, heads=
     lse = np.full((hq, tq), np.nan if restricted else -np.inf, dtype=np.float64)
     seqs = range(nseq) if seqs is None else seqs
     heads = range(hq) if heads is None else heads
+    thr = dropout_threshold(dropout_p)
     for s in seqs:
         qa, qb = int(cu_q[s]), int(cu_q[s + 1])
         ka, kb = int(cu_k[s]), int(cu_k[s + 1])
@@ -183,8 +195,16 @@ def attention(q, k, v, cu_q, cu_k, scale, mask_mode, window=0, seqs=None, heads=
                 g = h // grp
                 sc = scale * (q[r0:r1, h, :] @ k[ka:kb, g, :].T)
                 p, lse[h, r0:r1] = _softmax_rows(sc, a)
+                if thr > 0:
+                    p = p * _dropout_factor(seed, s, h, pq[r0:r1], pk[ka:kb], thr)
                 o[r0:r1, h, :] = p @ v[ka:kb, g, :]
     return o, lse
+
+
+def _dropout_factor(seed, s, h, pos_q, pos_k, thr):
+    """keep / (1 - t/256) for rows pos_q and columns pos_k of sequence s, head h."""
+    keep = dropout_keep(seed, s, h, pos_q[:, None], pos_k[None, :], thr)
+    return np.where(keep, 256.0 / (256.0 - thr), 0.0)
 
 
 def attention_per_sequence(q, k, v, cu_q, cu_k, scale, mask_mode, window=0):
@@ -210,30 +230,96 @@ def attention_per_sequence(q, k, v, cu_q, cu_k, scale, mask_mode, window=0):
 
 
 # ----------------------------------------------------------------------------------------
+# Dropout: a counter-based generator keyed by logical indices
+# ----------------------------------------------------------------------------------------
+
+_M32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+    as easy as 1, 2, 3", SC'11, section 3: the Philox S-box and its key schedule).
+
+    Each round multiplies counter words 0 and 2 by the two Philox multipliers (full 64-bit
+    products), and the new counter is (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+    lo(M0 c0)); the key is advanced by the two Weyl constants before every round but the
+    first. Counters broadcast as numpy arrays; returns four uint32 arrays.
+    """
+    m0, m1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
+    w0, w1 = np.uint64(0x9E3779B9), np.uint64(0xBB67AE85)
+    c = [np.asarray(x).astype(np.uint64) & _M32 for x in np.broadcast_arrays(c0, c1, c2, c3)]
+    k0 = np.uint64(int(k0) & 0xFFFFFFFF)
+    k1 = np.uint64(int(k1) & 0xFFFFFFFF)
+    for r in range(10):
+        if r:
+            k0 = (k0 + w0) & _M32
+            k1 = (k1 + w1) & _M32
+        p0 = m0 * c[0]  # < 2^64: exact in uint64
+        p1 = m1 * c[2]
+        c = [(p1 >> np.uint64(32)) ^ c[1] ^ k0, p1 & _M32, (p0 >> np.uint64(32)) ^ c[3] ^ k1,
+             p0 & _M32]
+    return [x.astype(np.uint32) for x in c]
+
+
+def dropout_threshold(p):
+    """Byte threshold t = round(256 p) of a dropout probability given as float32: an element
+    is dropped iff its random byte is below t, so the realised probability is t / 256.
+    t must be at most 255 (p < 255.5 / 256)."""
+    p32 = float(np.float32(p))
+    t = int(np.floor(p32 * 256.0 + 0.5))
+    if not (p32 >= 0.0 and t <= 255):
+        raise ValueError("dropout probability must lie in [0, 255.5/256)")
+    return t
+
+
+def dropout_keep(seed, seq, head, pos_q, pos_k, thr):
+    """Keep flags of (sequence index, query head, in-sequence positions) broadcast over
+    pos_q and pos_k. One generator call covers the 4 x 4 patch of query positions
+    4 (pos_q // 4) + 0..3 and key positions 4 (pos_k // 4) + 0..3: counter
+    (pos_q // 4, pos_k // 4, head, seq), key (low, high 32 bits of the 64-bit seed); the
+    element takes byte pos_k % 4 of output word pos_q % 4. Storage offsets never enter,
+    so the realisation replays across packings and in the backward."""
+    pos_q = np.asarray(pos_q, dtype=np.int64)
+    pos_k = np.asarray(pos_k, dtype=np.int64)
+    seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    w = philox4x32_10(pos_q // 4, pos_k // 4, int(head), int(seq), seed & 0xFFFFFFFF, seed >> 32)
+    qsel = np.broadcast_to(pos_q % 4, w[0].shape)
+    word = np.choose(qsel, w)
+    byte = (word >> (8 * (pos_k % 4)).astype(np.uint32)) & np.uint32(0xFF)
+    return byte >= np.uint32(thr)
+
+
+# ----------------------------------------------------------------------------------------
 # Backward: gradients of the same naive specification with the same mask
 # ----------------------------------------------------------------------------------------
 
-def _bwd_rows(qh, kg, vg, doh, a, scale):
+def _bwd_rows(qh, kg, vg, doh, a, scale, zf=None):
     """Gradients for one block of rows of one query head (all in float64).
 
     P is recomputed from the logits and the mask; D = rowsum(dO * O) with O = P V;
     dP = dO V^T; dS = P * (dP - D); dQ = scale dS K; dK = scale dS^T Q; dV = P^T dO.
+    With dropout factors zf (keep / (1 - p)): Z = P * zf, O = Z V, dZ = dO V^T,
+    dP = dZ * zf, dS = P * (dP - D) with D = rowsum(dO * O) = rowsum(P * dP), dV = Z^T dO.
     """
     s = scale * (qh @ kg.T)
     p, _ = _softmax_rows(s, a)
-    o = p @ vg
+    z = p if zf is None else p * zf
+    o = z @ vg
     dd = (doh * o).sum(axis=1)
     dp = doh @ vg.T
+    if zf is not None:
+        dp = dp * zf
     ds = p * (dp - dd[:, None])
-    return scale * (ds @ kg), scale * (ds.T @ qh), p.T @ doh
+    return scale * (ds @ kg), scale * (ds.T @ qh), z.T @ doh
 
 
 def attention_bwd(q, k, v, dout, cu_q, cu_k, scale, mask_mode, window=0,
-                  seqs=None, kv_heads=None):
+                  seqs=None, kv_heads=None, dropout_p=0.0, seed=0):
     """dQ [Tq,Hq,d], dK and dV [Tk,Hkv,d] (float64) of sum(dout * O).
 
     dK/dV of a K/V head are summed over every query head of its group. ``seqs`` /
-    ``kv_heads`` restrict the evaluation (other entries NaN).
+    ``kv_heads`` restrict the evaluation (other entries NaN). ``dropout_p`` / ``seed``
+    replay the forward's dropout realisation (the same keep flags).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -253,6 +339,7 @@ def attention_bwd(q, k, v, dout, cu_q, cu_k, scale, mask_mode, window=0,
     dv = np.full(v.shape, fill)
     seqs = range(len(lq)) if seqs is None else seqs
     kv_heads = range(hkv) if kv_heads is None else kv_heads
+    thr = dropout_threshold(dropout_p)
     for s in seqs:
         qa, qb = int(cu_q[s]), int(cu_q[s + 1])
         ka, kb = int(cu_k[s]), int(cu_k[s + 1])
@@ -264,8 +351,10 @@ def attention_bwd(q, k, v, dout, cu_q, cu_k, scale, mask_mode, window=0,
                     r1 = min(qb, r0 + _ROW_CHUNK)
                     a = allowed(sq[r0:r1, None], pq[r0:r1, None], sk[None, ka:kb],
                                 pk[None, ka:kb], lq[s], lk[s], mask_mode, window)
+                    zf = (_dropout_factor(seed, s, h, pq[r0:r1], pk[ka:kb], thr)
+                          if thr > 0 else None)
                     gq, gk, gv = _bwd_rows(q[r0:r1, h], k[ka:kb, g], v[ka:kb, g],
-                                           dout[r0:r1, h], a, scale)
+                                           dout[r0:r1, h], a, scale, zf)
                     dq[r0:r1, h] = gq
                     dk_acc += gk
                     dv_acc += gv
