@@ -20,8 +20,9 @@ ATTN_MASK_NONE, ATTN_MASK_CAUSAL_TOP_LEFT, ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1,
 ATTN_PATH_AUTO, ATTN_PATH_PREFILL, ATTN_PATH_SPLITK = 0, 1, 2
 
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_ex_workspace_size",
-           "attn_bwd", "attn_bwd_workspace_size", "attn_mask_probe", "attn_describe_plan",
-           "attn_status_string", "attn_version")
+           "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_dropout",
+           "attn_fwd_dropout_workspace_size", "attn_bwd_dropout", "attn_dropout_probe",
+           "attn_mask_probe", "attn_describe_plan", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -29,6 +30,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _F = ctypes.c_float
 _S = ctypes.c_size_t
+_U64 = ctypes.c_uint64
 
 
 class AttnError(RuntimeError):
@@ -65,6 +67,16 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_workspace_size.argtypes = [_I] * 11
     lib.attn_bwd_workspace_size.restype = _S
+    lib.attn_fwd_dropout.argtypes = [_P, _P, _P, _P, _P] + [_I] * 9 + [_F, _I, _I, _F, _U64,
+                                                                       _P, _P, _P, _S, _P]
+    lib.attn_fwd_dropout.restype = ctypes.c_int
+    lib.attn_fwd_dropout_workspace_size.argtypes = [_I] * 11
+    lib.attn_fwd_dropout_workspace_size.restype = _S
+    lib.attn_bwd_dropout.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P] + [_I] * 9 + \
+        [_F, _I, _I, _F, _U64, _P, _P, _P, _P, _S, _P]
+    lib.attn_bwd_dropout.restype = ctypes.c_int
+    lib.attn_dropout_probe.argtypes = [_I] * 6 + [_F, _U64, _P, _P]
+    lib.attn_dropout_probe.restype = ctypes.c_int
     lib.attn_mask_probe.argtypes = [_P, _P] + [_I] * 9 + [_P, _P]
     lib.attn_mask_probe.restype = ctypes.c_int
     lib.attn_describe_plan.argtypes = shape10 + [_I, _I, _I, ctypes.c_char_p, _S]
@@ -193,6 +205,67 @@ def attn_bwd(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
                          _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace.numel()), _stream())
     _check("attn_bwd", rc)
     return dq, dk, dv
+
+
+def attn_fwd_dropout(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
+                     mask_mode, window, dropout_p, seed, *, out=None, lse=None, workspace=None):
+    """Forward with dropout on the attention weights (attn_fwd_dropout in include/attn.h):
+    returns (out, lse); lse is that of the undropped softmax."""
+    _dev(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, workspace)
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    n, tq, tk, mq, mk, hq, hkv, d = _shape_args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k)
+    need = int(load().attn_fwd_dropout_workspace_size(n, tq, tk, mq, mk, hq, hkv, d,
+                                                      _dtype_code(q), int(mask_mode),
+                                                      int(window)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = load().attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k), n, tq, tk, mq, mk, hq, hkv, d,
+                                 _dtype_code(q), float(scale), int(mask_mode), int(window),
+                                 float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out),
+                                 _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream())
+    _check("attn_fwd_dropout", rc)
+    return out, lse
+
+
+def attn_bwd_dropout(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     max_seqlen_k, scale, mask_mode, window, dropout_p, seed, *, dq=None,
+                     dk=None, dv=None, workspace=None):
+    """Backward of attn_fwd_dropout with the same dropout_p and seed; returns (dq, dk, dv)."""
+    _dev(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_size(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, mask_mode,
+                                   window)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    n, tq, tk, mq, mk, hq, hkv, d = _shape_args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k)
+    rc = load().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), n, tq, tk, mq, mk, hq,
+                                 hkv, d, _dtype_code(q), float(scale), int(mask_mode),
+                                 int(window), float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 int(workspace.numel()), _stream())
+    _check("attn_bwd_dropout", rc)
+    return dq, dk, dv
+
+
+def attn_dropout_probe(seq, head, q0, nq, k0, nk, dropout_p, seed,
+                       device="cuda") -> torch.Tensor:
+    """uint8 [nq, nk]: 1 where the kernels keep element (q0+i, k0+j) of (seq, head)."""
+    keep = torch.empty((nq, nk), dtype=torch.uint8, device=device)
+    rc = load().attn_dropout_probe(int(seq), int(head), int(q0), int(nq), int(k0), int(nk),
+                                   float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                   _ptr(keep), _stream())
+    _check("attn_dropout_probe", rc)
+    return keep
 
 
 def attn_mask_probe(cu_seqlens_q, cu_seqlens_k, total_q, total_k, mask_mode, window, q0, nq,

@@ -159,6 +159,17 @@ FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu
   return a;
 }
 
+// Byte threshold t8 = round(256 p) and the keep scale 1 / (1 - t8 / 256) of a dropout
+// probability; false unless 0 <= p and t8 <= 255.
+bool dropout_threshold(float p, uint32_t* thr, float* scale) {
+  if (!(p >= 0.0f) || !std::isfinite(p)) return false;
+  const double t = std::floor((double)p * 256.0 + 0.5);
+  if (t > 255.0) return false;
+  *thr = (uint32_t)t;
+  *scale = (float)(256.0 / (256.0 - t));
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +190,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_BAD_SCALE: return "scale is not finite";
     case ATTN_ERR_BAD_PLAN: return "forced path or split count not usable for this shape";
     case ATTN_ERR_BAD_RANGE: return "probe window outside the token ranges";
+    case ATTN_ERR_BAD_DROPOUT: return "dropout probability not in [0, 255.5/256)";
     default: return "unknown status";
   }
 }
@@ -299,6 +311,101 @@ int attn_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs, 
   if (rc != ATTN_OK) return rc;
   hipError_t e = attn::launch_mask_probe(cu_q, cu_k, num_seqs, mode, window > 0 ? window : 0, q0,
                                          nq, k0, nk, bits, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
+}
+
+size_t attn_fwd_dropout_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                       int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv,
+                                       int32_t d, int32_t dtype, int32_t mode, int32_t window) {
+  return attn_fwd_ex_workspace_size(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype,
+                                    mode, window, ATTN_PATH_PREFILL, 0);
+}
+
+int attn_fwd_dropout(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                     const int32_t* cu_k, int32_t num_seqs, int32_t total_q, int32_t total_k,
+                     int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d,
+                     int32_t dtype, float scale, int32_t mode, int32_t window, float dropout_p,
+                     uint64_t seed, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                           window);
+  if (rc != ATTN_OK) return rc;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  uint32_t thr = 0;
+  float dscale = 1.0f;
+  if (!dropout_threshold(dropout_p, &thr, &dscale)) return ATTN_ERR_BAD_DROPOUT;
+  Plan plan;
+  rc = make_plan(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, ATTN_PATH_PREFILL,
+                 0, planning_cu_count(), &plan);
+  if (rc != ATTN_OK) return rc;
+  if (num_seqs == 0 || total_q == 0) return ATTN_OK;
+  if (!cu_q || !cu_k || !out || !lse || !q) return ATTN_ERR_NULL_PTR;
+  if (total_k > 0 && (!k || !v)) return ATTN_ERR_NULL_PTR;
+  if (plan.workspace > 0 && (!workspace)) return ATTN_ERR_NULL_PTR;
+  if (workspace_bytes < plan.workspace) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  rc = check_device();
+  if (rc != ATTN_OK) return rc;
+  FwdArgs a = make_args(q, k, v, cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k, hq, hkv,
+                        d, dtype, scale, mode, window, out, lse);
+  a.drop_thr = thr;
+  a.drop_scale = dscale;
+  a.seed = seed;
+  hipError_t e = attn::launch_fwd_prefill(a, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
+}
+
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, const int32_t* cu_q, const int32_t* cu_k,
+                     int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
+                     int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
+                     float scale, int32_t mode, int32_t window, float dropout_p, uint64_t seed,
+                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                           window);
+  if (rc != ATTN_OK) return rc;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  uint32_t thr = 0;
+  float dscale = 1.0f;
+  if (!dropout_threshold(dropout_p, &thr, &dscale)) return ATTN_ERR_BAD_DROPOUT;
+  const size_t need = attn::bwd_workspace_bytes(total_q, hq, d);
+  if (num_seqs == 0 || (total_q == 0 && total_k == 0)) return ATTN_OK;
+  if (!cu_q || !cu_k) return ATTN_ERR_NULL_PTR;
+  if (total_q > 0 && (!q || !out || !lse || !dout || !dq)) return ATTN_ERR_NULL_PTR;
+  if (total_k > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL_PTR;
+  if (need > 0 && !workspace) return ATTN_ERR_NULL_PTR;
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  rc = check_device();
+  if (rc != ATTN_OK) return rc;
+  attn::BwdArgs a;
+  a.f = make_args(q, k, v, cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d,
+                  dtype, scale, mode, window, nullptr, nullptr);
+  a.f.drop_thr = thr;
+  a.f.drop_scale = dscale;
+  a.f.seed = seed;
+  a.out = out;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  hipError_t e = attn::launch_bwd(a, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
+}
+
+int attn_dropout_probe(int32_t seq, int32_t head, int32_t q0, int32_t nq, int32_t k0,
+                       int32_t nk, float dropout_p, uint64_t seed, uint8_t* keep,
+                       void* stream) {
+  if (seq < 0 || head < 0 || q0 < 0 || nq < 0 || k0 < 0 || nk < 0) return ATTN_ERR_BAD_RANGE;
+  uint32_t thr = 0;
+  float dscale = 1.0f;
+  if (!dropout_threshold(dropout_p, &thr, &dscale)) return ATTN_ERR_BAD_DROPOUT;
+  if (nq == 0 || nk == 0) return ATTN_OK;
+  if (!keep) return ATTN_ERR_NULL_PTR;
+  int rc = check_device();
+  if (rc != ATTN_OK) return rc;
+  hipError_t e = attn::launch_dropout_probe(seed, thr, seq, head, q0, nq, k0, nk, keep,
+                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
 }
 

@@ -33,11 +33,15 @@ struct BwdParams {
   int mode, window;
   const float* lse2;   // [hq, total_q] LSE * log2(e); +inf for rows with no allowed key
   const float* dvec;   // [hq, total_q] rowsum(dO * O)
+  float* dvec_out;     // D written by the D pass (same buffer as dvec)
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
   int nslots, nlogical;        // key-tile slots (dK / dV kernel)
   int nslots_q, nlogical_q;    // query-tile slots (dQ kernel)
+  // dropout replay (kernels instantiated with DROP only): the forward's realisation
+  uint32_t seed_lo, seed_hi, drop_thr;
+  float drop_scale;
 };
 
 // Query positions [lo, hi) that see key position pk (the transpose of key_interval): from
@@ -123,7 +127,9 @@ struct BwdLds {
   static_assert(TOTAL <= LDS_BYTES, "backward tiles must fit in LDS");
 };
 
-template <int D>
+// With DROP, Z = P * keep / (1 - p) replaces P in dV, and dP = keep / (1 - p) * (dO V^T)
+// in dS = P * (dP - D); D = rowsum(dO * O) of the dropped output needs no change.
+template <int D, bool DROP = false>
 __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
   typedef Mma<__bf16, D> M;
   typedef BwdLds<D> L;
@@ -254,13 +260,32 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
         l4[a] = *reinterpret_cast<const f32x4*>(lse2s + 32 * qh + 8 * a + 4 * hg);
         d4[a] = *reinterpret_cast<const f32x4*>(dvs + 32 * qh + 8 * a + 4 * hg);
       }
+      if constexpr (DROP) {
+        const DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = qbase + (unsigned)(8 * (r >> 2) + (r & 3)) < qwidth;
-        const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[r >> 2][r & 3]));
-        const float pv = ok ? e : 0.0f;
-        sacc[r] = pv;
-        dpacc[r] = pv * (dpacc[r] - d4[r >> 2][r & 3]);
+        for (int a = 0; a < 4; ++a) {
+          // registers 4a..4a+3 hold queries qa + 8 a + 4 hg + 0..3 against key kj
+          const uint32_t keep = dropout_keep_col(drop, (qa + 8 * a + 4 * hg) >> 2, kj);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int r = 4 * a + b;
+            const bool ok = qbase + (unsigned)(8 * a + b) < qwidth;
+            const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[a][b]));
+            const float pv = ok ? e : 0.0f;
+            const bool kept = (keep >> b) & 1u;
+            sacc[r] = kept ? pv * drop.scale : 0.0f;
+            dpacc[r] = pv * ((kept ? dpacc[r] * drop.scale : 0.0f) - d4[a][b]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = qbase + (unsigned)(8 * (r >> 2) + (r & 3)) < qwidth;
+          const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[r >> 2][r & 3]));
+          const float pv = ok ? e : 0.0f;
+          sacc[r] = pv;
+          dpacc[r] = pv * (dpacc[r] - d4[r >> 2][r & 3]);
+        }
       }
       M::pack_p(sacc, pp[0]);
       M::pack_p(dpacc, pd[0]);
@@ -321,7 +346,12 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
 //   dQ^T += K^T dS^T               (the forward's PV contraction with K in place of V).
 // dQ = scale * acc is written once, in the output type: no atomics, no fp32 workspace.
 // ---------------------------------------------------------------------------------------
-template <int D>
+// DONLY (dropout backward only): instead of dQ, compute D = sum_j P dP of every query row
+// in fp32 (dP carrying the keep / (1 - p) factor) and write it over the D that bwd_pre
+// formed from the stored output. Both equal rowsum(dO * O) for the exact O; with dropout
+// even a one-key row stores a rounded 1.25 v, whose rounding no longer cancels in
+// dS = P (dP - D) and would move dK of such keys far beyond the gradient tolerance.
+template <int D, bool DROP = false, bool DONLY = false>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   typedef Mma<__bf16, D> M;
   constexpr int BM = FWD_BM, BN = FWD_BN, ROWB = M::ROWB, TILE = BN * ROWB;
@@ -354,7 +384,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   M::load_q(dor, p.dout + qoff, qvalid, false, lane);
   const size_t li = (size_t)h * p.total_q + g.q_start + pq;
   const float l2 = qvalid ? p.lse2[li] : __builtin_inff();
-  const float dvl = qvalid ? p.dvec[li] : 0.0f;
+  const float dvl = (!DONLY && qvalid) ? p.dvec[li] : 0.0f;
+  float dsum = 0.0f;  // DONLY: this lane's part of sum_j P dP
   const typename M::Offsets of = M::offsets(lane);
 
   int klo, khi;
@@ -385,16 +416,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
       M::qk(sacc, kt + kb * 32 * ROWB, qr, of, lane);
       M::qk(dpacc, vt + kb * 32 * ROWB, dor, of, lane);
+      if constexpr (DROP) {
+        const DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = kbase + (unsigned)(32 * kb + 8 * (r >> 2) + (r & 3)) < kwidth;
-        const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));  // computed, then selected
-        const float pv = ok ? e : 0.0f;
-        sacc[r] = pv * (dpacc[r] - dvl);
+        for (int a = 0; a < 4; ++a) {
+          // registers 4a..4a+3 hold keys k0 + 32 kb + 8 a + 4 hg + 0..3 against query pq
+          const uint32_t keep = dropout_keep_row(drop, pq, (k0 + 32 * kb + 8 * a + 4 * hg) >> 2);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int r = 4 * a + b;
+            const bool ok = kbase + (unsigned)(32 * kb + 8 * a + b) < kwidth;
+            const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));
+            const float pv = ok ? e : 0.0f;
+            const float dpz = ((keep >> b) & 1u) ? dpacc[r] * drop.scale : 0.0f;
+            if constexpr (DONLY)
+              dsum = fmaf(pv, dpz, dsum);
+            else
+              sacc[r] = pv * (dpz - dvl);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = kbase + (unsigned)(32 * kb + 8 * (r >> 2) + (r & 3)) < kwidth;
+          const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));  // computed, then selected
+          const float pv = ok ? e : 0.0f;
+          sacc[r] = pv * (dpacc[r] - dvl);
+        }
       }
-      typename M::PPack pk;
-      M::pack_p(sacc, pk);
-      M::pv(acc, pk, kt + kb * 32 * ROWB, of, lane);
+      if constexpr (!DONLY) {
+        typename M::PPack pk;
+        M::pack_p(sacc, pk);
+        M::pv(acc, pk, kt + kb * 32 * ROWB, of, lane);
+      }
     }
   };
 
@@ -424,6 +478,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     }
   }
 
+  if constexpr (DONLY) {
+    // lanes l and l ^ 32 hold the same query over different keys
+    const float dtot = sum_halves(dsum);
+    if (qvalid && lane < 32) p.dvec_out[li] = dtot;
+    return;
+  }
   // dQ = scale * acc; accumulator column = query, rows = head dim.
   if (qvalid) {
     __bf16* dst = p.dq + qoff;
@@ -487,15 +547,33 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   p.nlogical = p.nslots * f.hkv;
   p.nslots_q = f.total_q / FWD_BM + f.num_seqs;
   p.nlogical_q = p.nslots_q * f.hq;
+  const bool drop = f.drop_thr > 0;
+  p.seed_lo = (uint32_t)f.seed;
+  p.seed_hi = (uint32_t)(f.seed >> 32);
+  p.drop_thr = f.drop_thr;
+  p.drop_scale = f.drop_scale;
+  p.dvec_out = dvec;
+  if (drop && f.total_q > 0) {
+    const int grid = ((p.nlogical_q + 7) / 8) * 8;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3(grid), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (f.total_k > 0) {
     const int grid = ((p.nlogical + 7) / 8) * 8;
-    hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(grid), dim3(512), 0, st, p);
+    if (drop)
+      hipLaunchKernelGGL((bwd_main_kernel<D, true>), dim3(grid), dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(grid), dim3(512), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (f.total_q > 0) {
     const int grid = ((p.nlogical_q + 7) / 8) * 8;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(grid), dim3(256), 0, st, p);
+    if (drop)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(grid), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }

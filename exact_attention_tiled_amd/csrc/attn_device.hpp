@@ -206,6 +206,79 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nlogical) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Dropout on the attention weights. The realisation must replay in the backward and
+// across packings, so it is a function of logical indices only (Causal Mask and Ragged
+// Sequence Layouts, section 6): the keep flag of (sequence index s, query head h,
+// in-sequence query position i, key position j) is byte j % 4 of output word i % 4 of
+// Philox4x32-10 at counter (i / 4, j / 4, h, s) under the 64-bit seed, kept iff the byte
+// is at least thr = round(256 p). One generator call thus serves a 4 x 4 patch: the
+// forward and dQ kernels (queries on lanes, 4 consecutive keys per register group) use one
+// word of it, the dK/dV kernel (keys on lanes, 4 consecutive queries per group) one byte
+// of each word.
+// ---------------------------------------------------------------------------------------
+struct DropoutSite {
+  uint32_t seed_lo, seed_hi;
+  uint32_t thr;    // 1..255 (0: no dropout; the kernels without it never read this)
+  float scale;     // 1 / (1 - thr / 256)
+  int s, h;        // sequence index, query head
+};
+
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): per round two 32 x 32 -> 64-bit products of counter words 0
+// and 2 with the Philox multipliers, the new counter (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1,
+// lo0), and the key advanced by the two Weyl constants before every round but the first.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[1] = (uint32_t)p1;
+    c[3] = (uint32_t)p0;
+    c[0] = n0;
+    c[2] = n2;
+  }
+}
+
+// The patch of query positions 4 qp + 0..3 and key positions 4 kp + 0..3: w[a] holds
+// query 4 qp + a, its byte b key 4 kp + b.
+__device__ __forceinline__ void dropout_patch(const DropoutSite& d, int qp, int kp,
+                                              uint32_t (&w)[4]) {
+  w[0] = (uint32_t)qp;
+  w[1] = (uint32_t)kp;
+  w[2] = (uint32_t)d.h;
+  w[3] = (uint32_t)d.s;
+  philox4x32_10(w, d.seed_lo, d.seed_hi);
+}
+
+// The 4 keep flags (bit b: key 4 kp + b) of query position pq against keys 4 kp + 0..3.
+__device__ __forceinline__ uint32_t dropout_keep_row(const DropoutSite& d, int pq, int kp) {
+  uint32_t w[4];
+  dropout_patch(d, pq >> 2, kp, w);
+  const uint32_t x = (pq & 2) ? ((pq & 1) ? w[3] : w[2]) : ((pq & 1) ? w[1] : w[0]);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) bits |= (((x >> (8 * b)) & 0xFFu) >= d.thr ? 1u : 0u) << b;
+  return bits;
+}
+
+// The 4 keep flags (bit a: query 4 qp + a) of key position pk against queries 4 qp + 0..3.
+__device__ __forceinline__ uint32_t dropout_keep_col(const DropoutSite& d, int qp, int pk) {
+  uint32_t w[4];
+  dropout_patch(d, qp, pk >> 2, w);
+  const int sh = 8 * (pk & 3);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) bits |= (((w[a] >> sh) & 0xFFu) >= d.thr ? 1u : 0u) << a;
+  return bits;
+}
+
+// ---------------------------------------------------------------------------------------
 // Swizzled LDS tiles filled by buffer -> LDS DMA.
 //
 // A tile row r of ROWB bytes occupies [r * ROWB, (r + 1) * ROWB) with its 16-byte chunk c

@@ -38,6 +38,9 @@ struct FwdParams {
   float* part_o;
   float* part_lse;
   int blocks_per_kvh, chunk, nsplit;
+  // dropout (prefill kernel instantiated with DROP only)
+  uint32_t seed_lo, seed_hi, drop_thr;
+  float drop_scale;
 };
 
 // The exponent offset of a row moves only when a tile's maximum exceeds it by more than
@@ -51,11 +54,14 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 // kpos0 + 32 kb + key_of_reg(r, g); pk receives P (not yet normalised) as the PV operand.
 // m_run is in log2 units of the scaled logits; l_run is this lane's partial denominator
 // (the other half of the row lives in lane l ^ 32).
-template <typename M, int NK, int D>
+// With DROP the denominator still sums every weight, and the PV operand carries
+// weight * keep / (1 - p) (the keep flags of DropoutSite for this lane's query).
+template <typename M, int NK, int D, bool DROP = false>
 __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack (&pk)[NK],
                                              bool need_mask, int pq, int kpos0, const SeqGeom& g,
                                              int mode, int window, float c2, float& m_run,
-                                             float& l_run, f32x16 (&o)[D / 32], int lane) {
+                                             float& l_run, f32x16 (&o)[D / 32], int lane,
+                                             const DropoutSite& drop = DropoutSite{}) {
   if (need_mask) mask_blocks<NK>(s, pq, kpos0, g, mode, window, lane);
   float mx = neg_inf();
 #pragma unroll
@@ -90,8 +96,28 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack 
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(fmaf(s[kb][r], c2, -base));
   }
+  if constexpr (DROP) {
+    const int hg = lane >> 5;
 #pragma unroll
-  for (int kb = 0; kb < NK; ++kb) l_run += M::pack_p(s[kb], pk[kb]);
+    for (int kb = 0; kb < NK; ++kb) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += s[kb][r];
+      l_run += sum;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        // registers 4a..4a+3 hold keys kpos0 + 32 kb + 8 a + 4 hg + 0..3
+        const uint32_t keep = dropout_keep_row(drop, pq, (kpos0 + 32 * kb + 8 * a + 4 * hg) >> 2);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          s[kb][4 * a + b] = ((keep >> b) & 1u) ? s[kb][4 * a + b] * drop.scale : 0.0f;
+      }
+      (void)M::pack_p(s[kb], pk[kb]);
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) l_run += M::pack_p(s[kb], pk[kb]);
+  }
 }
 
 // The (query head, sequence, query tile) of this workgroup; false for padding blocks.
@@ -144,7 +170,7 @@ __device__ __forceinline__ bool prefill_tile(const FwdParams& p, int& h, int& s,
 }
 
 // Running state of one prefill wave (32 query rows) and its step over one 64-key stage.
-template <typename T, int D>
+template <typename T, int D, bool DROP = false>
 struct PrefillWave {
   typedef Mma<T, D> M;
   f32x16 o[D / 32];
@@ -163,7 +189,8 @@ struct PrefillWave {
   __device__ __forceinline__ void stage(const char* kt, const char* vt, int k0, int wp0, int wp1,
                                         int pq, const SeqGeom& g, const FwdParams& p,
                                         const typename M::QOperand (&qr)[M::QREGS],
-                                        const typename M::Offsets& of, int lane) {
+                                        const typename M::Offsets& of, int lane,
+                                        const DropoutSite& drop) {
     constexpr int ROWB = M::ROWB;
     const int cls = block_class(wp0, wp1, k0, k0 + FWD_BN, g, p.mode, p.window);
     if (cls == 0) return;
@@ -184,8 +211,8 @@ struct PrefillWave {
     }
     __builtin_amdgcn_s_setprio(0);
     typename M::PPack pk[2];
-    softmax_step<M, 2, D>(sacc, pk, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run, l_run, o,
-                          lane);
+    softmax_step<M, 2, D, DROP>(sacc, pk, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run,
+                                l_run, o, lane, drop);
     __builtin_amdgcn_s_setprio(1);
     if constexpr (std::is_same<T, __bf16>::value) {
       M::pv2(o, pk, vt, of);
@@ -230,7 +257,9 @@ struct PrefillVStage<__bf16, D> {
 // waves share each 64-key K/V stage. Stages are DMA'd into two LDS buffers in turn: the
 // load of stage j+1 is in flight while stage j is computed.
 // ---------------------------------------------------------------------------------------
-template <typename T, int D>
+// With DROP the weights reaching V carry the dropout realisation (DropoutSite); this
+// kernel is the forward of every dropout call.
+template <typename T, int D, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   typedef Mma<T, D> M;
   constexpr int BM = FWD_BM, BN = FWD_BN, ROWB = M::ROWB;
@@ -270,8 +299,10 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   PrefillVStage<T, D> vst;
   vst.init(wave, lane, tid, rstride);
 
-  PrefillWave<T, D> st;
+  PrefillWave<T, D, DROP> st;
   st.init();
+  DropoutSite drop{};
+  if constexpr (DROP) drop = DropoutSite{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
 
   // Stage j lives in buffer j % 2. The loads of stage j+1 are issued before stage j is
   // computed; the barrier after stage j publishes stage j+1 (the V^T transpose-write happens
@@ -289,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
       dma.issue(kb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, kbuf1);
       vst.issue(vb0 + (size_t)(k0 + BN) * rstride, g.len_k - k0 - BN, rstride, vbuf1);
     }
-    st.stage(kbuf0, vbuf0, k0, wp0, wp1, pq, g, p, qr, of, lane);
+    st.stage(kbuf0, vbuf0, k0, wp0, wp1, pq, g, p, qr, of, lane, drop);
     wait_vmem();
     if (it + 1 < nst) vst.commit(vbuf1);
     __syncthreads();
@@ -298,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
         dma.issue(kb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, kbuf0);
         vst.issue(vb0 + (size_t)(k0 + 2 * BN) * rstride, g.len_k - k0 - 2 * BN, rstride, vbuf0);
       }
-      st.stage(kbuf1, vbuf1, k0 + BN, wp0, wp1, pq, g, p, qr, of, lane);
+      st.stage(kbuf1, vbuf1, k0 + BN, wp0, wp1, pq, g, p, qr, of, lane, drop);
       wait_vmem();
       if (it + 2 < nst) vst.commit(vbuf0);
       __syncthreads();
@@ -908,6 +939,16 @@ __global__ void mask_probe_kernel(const int32_t* cu_q, const int32_t* cu_k, int 
   bits[idx] = bit;
 }
 
+// keep[i * nk + j] = 1 iff element (query position q0 + i, key position k0 + j) of sequence
+// d.s, head d.h survives dropout: the same DropoutSite functions the kernels use.
+__global__ void dropout_probe_kernel(DropoutSite d, int q0, int nq, int k0, int nk,
+                                     uint8_t* keep) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)nq * nk) return;
+  const int i = q0 + (int)(idx / nk), j = k0 + (int)(idx % nk);
+  keep[idx] = (uint8_t)((dropout_keep_row(d, i, j >> 2) >> (j & 3)) & 1u);
+}
+
 // ---------------------------------------------------------------------------------------
 // Tile order of a prefill over sequences of different lengths. Every (sequence, query
 // tile) slot gets its cost - the number of 64-key stages its rows visit - and the slots
@@ -1057,10 +1098,17 @@ static hipError_t prefill_typed(const FwdArgs& a, void* ws, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const int grid = fwd_prefill_grid(a);
-  if constexpr (std::is_same<T, __bf16>::value)
+  if (a.drop_thr > 0) {
+    p.seed_lo = (uint32_t)a.seed;
+    p.seed_hi = (uint32_t)(a.seed >> 32);
+    p.drop_thr = a.drop_thr;
+    p.drop_scale = a.drop_scale;
+    hipLaunchKernelGGL((fwd_prefill_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
+  } else if constexpr (std::is_same<T, __bf16>::value) {
     hipLaunchKernelGGL((fwd_prefill_bf16_kernel<D>), dim3(grid), dim3(256), 0, st, p);
-  else
+  } else {
     hipLaunchKernelGGL((fwd_prefill_kernel<T, D>), dim3(grid), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -1117,6 +1165,15 @@ hipError_t launch_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int num_s
   const int grid = (int)((n + 255) / 256);
   hipLaunchKernelGGL(mask_probe_kernel, dim3(grid), dim3(256), 0, st, cu_q, cu_k, num_seqs, mode,
                      window, q0, nq, k0, nk, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_dropout_probe(uint64_t seed, uint32_t thr, int s, int h, int q0, int nq, int k0,
+                                int nk, uint8_t* keep, hipStream_t st) {
+  const DropoutSite d{(uint32_t)seed, (uint32_t)(seed >> 32), thr, 1.0f, s, h};
+  const long n = (long)nq * nk;
+  hipLaunchKernelGGL(dropout_probe_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, d,
+                     q0, nq, k0, nk, keep);
   return hipGetLastError();
 }
 

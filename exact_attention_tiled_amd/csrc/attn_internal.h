@@ -19,6 +19,11 @@ struct FwdArgs {
   int mode, window;
   void* out;
   float* lse;
+  // dropout on the attention weights: thr = round(256 p) in 1..255 (0 = none), scale =
+  // 1 / (1 - thr / 256), 64-bit seed of the counter-based generator
+  uint32_t drop_thr = 0;
+  float drop_scale = 1.0f;
+  uint64_t seed = 0;
 };
 
 struct BwdArgs {
@@ -47,6 +52,9 @@ int fwd_prefill_grid(const FwdArgs& a);
 // workspace: one int32 per slot).
 size_t fwd_prefill_workspace_bytes(const FwdArgs& a);
 hipError_t launch_fwd_prefill(const FwdArgs& a, void* workspace, hipStream_t stream);
+// keep[i * nk + j] (uint8) of dropout element (q0 + i, k0 + j) of sequence s, query head h.
+hipError_t launch_dropout_probe(uint64_t seed, uint32_t thr, int s, int h, int q0, int nq, int k0,
+                                int nk, uint8_t* keep, hipStream_t stream);
 
 // Partials per key chunk of the split-K path (the waves of a workgroup merge theirs).
 int splitk_partials_per_chunk(int rows);

@@ -67,7 +67,8 @@ typedef enum attn_status {
   ATTN_ERR_LAUNCH_FAILED = -8,        /* the HIP runtime rejected a kernel launch */
   ATTN_ERR_BAD_SCALE = -9,            /* scale is not finite */
   ATTN_ERR_BAD_PLAN = -10,            /* forced path / split count not usable for the shape */
-  ATTN_ERR_BAD_RANGE = -11            /* mask probe window outside the token ranges */
+  ATTN_ERR_BAD_RANGE = -11,           /* probe window outside the token ranges */
+  ATTN_ERR_BAD_DROPOUT = -12          /* dropout probability not in [0, 255.5/256) */
 } attn_status;
 
 enum attn_dtype { ATTN_BF16 = 0, ATTN_F32 = 1 };
@@ -155,6 +156,63 @@ size_t attn_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_
                                int32_t max_seqlen_q, int32_t max_seqlen_k,
                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                                int32_t dtype, int32_t mask_mode, int32_t window);
+
+/*
+ * attn_fwd_dropout / attn_bwd_dropout - attn_fwd / attn_bwd with inverted dropout on the
+ * attention weights. Dropout is a separate contract from the deterministic operator
+ * (Attention Algorithm Error and Complexity Tests, section 1) whose realisation replays in
+ * the backward and across packings by logical index (Causal Mask and Ragged Sequence
+ * Layouts, section 6; same first page, section 4: gradients use the same realisation):
+ *     O[t,h,:] = sum_u p(t,u) keep(s,h,i,j) / (1 - t8/256) V[u,g,:]
+ * with p(t,u) and LSE exactly as for attn_fwd (the LSE is that of the undropped softmax).
+ * keep(s,h,i,j) for sequence index s, query head h, in-sequence query position i and key
+ * position j: byte j % 4 of output word i % 4 of Philox4x32-10 (Salmon et al., SC'11) at
+ * counter (i / 4, j / 4, h, s) and key (seed & 0xffffffff, seed >> 32), kept iff that byte
+ * is >= t8 = floor(256 * dropout_p + 0.5) (computed in double from the float argument).
+ *   dropout_p   in [0, 255.5/256), else ATTN_ERR_BAD_DROPOUT; t8 = 0 runs attn_fwd /
+ *               attn_bwd unchanged
+ *   seed        any 64-bit value; attn_bwd_dropout must get the forward's dropout_p and seed
+ * The forward always runs the prefill path (bf16 or fp32) and needs the workspace of
+ * attn_fwd_dropout_workspace_size; the backward is bf16 only (like attn_bwd) and needs
+ * attn_bwd_workspace_size. Other arguments, ownership and errors as attn_fwd / attn_bwd.
+ */
+int attn_fwd_dropout(const void* q, const void* k, const void* v,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                     int32_t num_seqs, int32_t total_q, int32_t total_k,
+                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t dtype,
+                     float scale, int32_t mask_mode, int32_t window,
+                     float dropout_p, uint64_t seed,
+                     void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+size_t attn_fwd_dropout_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                       int32_t num_heads_q, int32_t num_heads_kv,
+                                       int32_t head_dim, int32_t dtype, int32_t mask_mode,
+                                       int32_t window);
+
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                     int32_t num_seqs, int32_t total_q, int32_t total_k,
+                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t dtype,
+                     float scale, int32_t mask_mode, int32_t window,
+                     float dropout_p, uint64_t seed,
+                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * attn_dropout_probe - runs the kernels' dropout realisation for sequence index seq and
+ * query head head over in-sequence positions [q0, q0 + nq) x [k0, k0 + nk) and writes
+ * keep[i * nk + j] = 1 if element (q0 + i, k0 + j) is kept, else 0 (uint8, device memory,
+ * nq * nk bytes). Exists so the realisation can be tested bit-exactly. Positions are not
+ * checked against any sequence length. Returns ATTN_ERR_BAD_RANGE for negative arguments.
+ */
+int attn_dropout_probe(int32_t seq, int32_t head, int32_t q0, int32_t nq, int32_t k0,
+                       int32_t nk, float dropout_p, uint64_t seed, uint8_t* keep,
+                       void* stream);
 
 /*
  * attn_mask_probe - runs the forward kernels' mask unit (tile range selection plus the

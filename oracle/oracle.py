@@ -273,18 +273,22 @@ def dropout_threshold(p):
 
 
 def dropout_keep(seed, seq, head, pos_q, pos_k, thr):
-    """Keep flags of (sequence index, query head, in-sequence positions) broadcast over
-    pos_q and pos_k. One generator call covers the 4 x 4 patch of query positions
-    4 (pos_q // 4) + 0..3 and key positions 4 (pos_k // 4) + 0..3: counter
-    (pos_q // 4, pos_k // 4, head, seq), key (low, high 32 bits of the 64-bit seed); the
-    element takes byte pos_k % 4 of output word pos_q % 4. Storage offsets never enter,
-    so the realisation replays across packings and in the backward."""
+    """Keep flags [n, m] of (sequence index, query head) for query positions pos_q (shape
+    [n, 1]) against key positions pos_k (shape [1, m]). One generator call covers the 4 x 4
+    patch of query positions 4 (pos_q // 4) + 0..3 and key positions 4 (pos_k // 4) + 0..3:
+    counter (pos_q // 4, pos_k // 4, head, seq), key (low, high 32 bits of the 64-bit
+    seed); the element takes byte pos_k % 4 of output word pos_q % 4. Storage offsets never
+    enter, so the realisation replays across packings and in the backward."""
     pos_q = np.asarray(pos_q, dtype=np.int64)
     pos_k = np.asarray(pos_k, dtype=np.int64)
+    if pos_q.ndim != 2 or pos_k.ndim != 2 or pos_q.shape[1] != 1 or pos_k.shape[0] != 1:
+        raise ValueError("pos_q must be [n, 1] and pos_k [1, m]")
     seed = int(seed) & 0xFFFFFFFFFFFFFFFF
-    w = philox4x32_10(pos_q // 4, pos_k // 4, int(head), int(seq), seed & 0xFFFFFFFF, seed >> 32)
-    qsel = np.broadcast_to(pos_q % 4, w[0].shape)
-    word = np.choose(qsel, w)
+    qp, iq = np.unique(pos_q[:, 0] // 4, return_inverse=True)
+    kp, ik = np.unique(pos_k[0, :] // 4, return_inverse=True)
+    words = np.stack(philox4x32_10(qp[:, None], kp[None, :], int(head), int(seq),
+                                   seed & 0xFFFFFFFF, seed >> 32))        # [4, patches_q, patches_k]
+    word = words[(pos_q % 4), iq[:, None], ik[None, :]]
     byte = (word >> (8 * (pos_k % 4)).astype(np.uint32)) & np.uint32(0xFF)
     return byte >= np.uint32(thr)
 
@@ -293,18 +297,19 @@ def dropout_keep(seed, seq, head, pos_q, pos_k, thr):
 # Backward: gradients of the same naive specification with the same mask
 # ----------------------------------------------------------------------------------------
 
-def _bwd_rows(qh, kg, vg, doh, a, scale, zf=None):
+def _bwd_rows(qh, kg, vg, doh, a, scale, zf=None, oh=None):
     """Gradients for one block of rows of one query head (all in float64).
 
     P is recomputed from the logits and the mask; D = rowsum(dO * O) with O = P V;
     dP = dO V^T; dS = P * (dP - D); dQ = scale dS K; dK = scale dS^T Q; dV = P^T dO.
     With dropout factors zf (keep / (1 - p)): Z = P * zf, O = Z V, dZ = dO V^T,
     dP = dZ * zf, dS = P * (dP - D) with D = rowsum(dO * O) = rowsum(P * dP), dV = Z^T dO.
+    With a stored output oh, D = rowsum(dO * oh) instead.
     """
     s = scale * (qh @ kg.T)
     p, _ = _softmax_rows(s, a)
     z = p if zf is None else p * zf
-    o = z @ vg
+    o = z @ vg if oh is None else oh
     dd = (doh * o).sum(axis=1)
     dp = doh @ vg.T
     if zf is not None:
@@ -314,17 +319,23 @@ def _bwd_rows(qh, kg, vg, doh, a, scale, zf=None):
 
 
 def attention_bwd(q, k, v, dout, cu_q, cu_k, scale, mask_mode, window=0,
-                  seqs=None, kv_heads=None, dropout_p=0.0, seed=0):
+                  seqs=None, kv_heads=None, dropout_p=0.0, seed=0, out=None):
     """dQ [Tq,Hq,d], dK and dV [Tk,Hkv,d] (float64) of sum(dout * O).
 
     dK/dV of a K/V head are summed over every query head of its group. ``seqs`` /
     ``kv_heads`` restrict the evaluation (other entries NaN). ``dropout_p`` / ``seed``
     replay the forward's dropout realisation (the same keep flags).
+
+    ``out`` ([Tq, Hq, d], optional): the stored forward output the backward is given (the
+    library's backward receives the forward's output as an input); D = rowsum(dout * out)
+    is then formed from it instead of from the oracle's own float64 output. Everything else
+    is unchanged.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
+    out = None if out is None else np.asarray(out, dtype=np.float64)
     tq, hq, d = q.shape
     tk, hkv, _ = k.shape
     if hq % hkv != 0:
@@ -354,7 +365,8 @@ def attention_bwd(q, k, v, dout, cu_q, cu_k, scale, mask_mode, window=0,
                     zf = (_dropout_factor(seed, s, h, pq[r0:r1], pk[ka:kb], thr)
                           if thr > 0 else None)
                     gq, gk, gv = _bwd_rows(q[r0:r1, h], k[ka:kb, g], v[ka:kb, g],
-                                           dout[r0:r1, h], a, scale, zf)
+                                           dout[r0:r1, h], a, scale, zf,
+                                           None if out is None else out[r0:r1, h])
                     dq[r0:r1, h] = gq
                     dk_acc += gk
                     dv_acc += gv

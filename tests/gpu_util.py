@@ -77,3 +77,4 @@ def check_fwd(w, out, lse, ref_o, ref_lse, what=""):
     atol, rtol = tol_for(w)
     assert_close(to_np(out), ref_o, atol, rtol, f"{what} O")
     assert_close(to_np(lse), ref_lse, LSE_TOL, 0.0, f"{what} LSE")
+

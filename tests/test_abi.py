@@ -12,7 +12,7 @@ from exact_attention_tiled_amd import build as eat_build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 OK, NULL_PTR, BAD_SHAPE, BAD_HEADS, BAD_DTYPE, BAD_MASK, WS_SMALL = 0, -1, -2, -3, -4, -5, -6
-BAD_SCALE, BAD_PLAN, BAD_RANGE = -9, -10, -11
+BAD_SCALE, BAD_PLAN, BAD_RANGE, BAD_DROPOUT = -9, -10, -11, -12
 
 
 @pytest.fixture(scope="module")
@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_status_strings(lib):
     assert eat.attn_version() == 100
     for code in (OK, NULL_PTR, BAD_SHAPE, BAD_HEADS, BAD_DTYPE, BAD_MASK, WS_SMALL, -7, -8,
-                 BAD_SCALE, BAD_PLAN, BAD_RANGE):
+                 BAD_SCALE, BAD_PLAN, BAD_RANGE, BAD_DROPOUT):
         s = eat.attn_status_string(code)
         assert s and s != "unknown status"
     assert eat.attn_status_string(12345) == "unknown status"
@@ -118,3 +118,33 @@ def test_build_command_targets_gfx950():
     cmd = eat_build.compile_command("/tmp/x.so")
     assert "--offload-arch=gfx950" in cmd
     assert "-packed-fp32-ops" in cmd
+
+
+def test_dropout_validation(lib):
+    """Dropout probabilities outside [0, 255.5/256) (or not finite) are rejected before any
+    launch; the other arguments are validated as for attn_fwd / attn_bwd."""
+    f = ctypes.c_float
+
+    def fwd(p, **kw):
+        a = dict(q=1, k=1, v=1, cu_q=1, cu_k=1, d=64, out=1, lse=1, ws=None, wsb=0)
+        a.update(kw)
+        return lib.attn_fwd_dropout(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], 1, 4, 4, 4, 4,
+                                    2, 1, a["d"], 0, f(0.125), 1, 0, f(p), 12345, a["out"],
+                                    a["lse"], a["ws"], a["wsb"], None)
+
+    for p in (1.0, -0.1, 255.6 / 256, float("nan"), float("inf")):
+        assert fwd(p) == BAD_DROPOUT, p
+    assert fwd(0.1, d=96) == BAD_SHAPE
+    assert fwd(0.1, out=None) == NULL_PTR
+    bargs = [1] * 8 + [1, 4, 4, 4, 4, 2, 1, 64, 0, f(0.1), 1, 0, f(1.5), 7, 1, 1, 1, None, 0,
+                       None]
+    assert lib.attn_bwd_dropout(*bargs) == BAD_DROPOUT
+    bargs[20] = f(0.2)
+    bargs[23] = None   # dk
+    assert lib.attn_bwd_dropout(*bargs) == NULL_PTR
+    assert lib.attn_fwd_dropout_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 0, 1, 0) == 0
+    assert lib.attn_fwd_dropout_workspace_size(2, 9, 9, 5, 5, 2, 1, 64, 0, 1, 0) > 0  # ragged
+    assert lib.attn_dropout_probe(0, 0, -1, 4, 0, 4, f(0.1), 1, None, None) == BAD_RANGE
+    assert lib.attn_dropout_probe(0, 0, 0, 4, 0, 4, f(1.0), 1, None, None) == BAD_DROPOUT
+    assert lib.attn_dropout_probe(0, 0, 0, 0, 0, 4, f(0.1), 1, None, None) == OK
+    assert lib.attn_dropout_probe(0, 0, 0, 4, 0, 4, f(0.1), 1, None, None) == NULL_PTR

@@ -1,0 +1,171 @@
+"""GPU parity of attention dropout: the kernels' realisation bit-exactly against the oracle's,
+and forward / backward against the fp64 oracle replaying the same realisation."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import BF16_TOL, LSE_TOL, assert_close, to_device, to_np, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    import exact_attention_tiled_amd as eat
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    eat.load()
+
+
+def fwd_drop(w, t, p, seed):
+    import exact_attention_tiled_amd as eat
+    return eat.attn_fwd_dropout(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q,
+                                w.max_seqlen_k, w.scale, w.mask_mode, w.window, p, seed)
+
+
+def bwd_drop(w, t, out, lse, p, seed):
+    import exact_attention_tiled_amd as eat
+    return eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out, lse, t["dout"], t["cu_q"],
+                                t["cu_k"], w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
+                                w.window, p, seed)
+
+
+@pytest.mark.parametrize("seed,p,seq,head,q0,nq,k0,nk", [
+    (0, 0.1, 0, 0, 0, 64, 0, 64),
+    (0x0123456789ABCDEF, 0.5, 3, 7, 5, 37, 2, 91),
+    (2**64 - 1, 0.9, 16383, 31, 131000, 40, 130950, 120),
+    (42, 1.0 / 256, 1, 2, 1, 3, 1, 3),
+    (42, 255.0 / 256, 1, 2, 0, 16, 0, 16),
+])
+def test_dropout_probe_bit_exact(seed, p, seq, head, q0, nq, k0, nk):
+    """The kernels' keep flags equal the oracle's element for element (integer work)."""
+    import exact_attention_tiled_amd as eat
+    print(f"dropout probe seed={seed} p={p} seq={seq} head={head}", flush=True)
+    got = eat.attn_dropout_probe(seq, head, q0, nq, k0, nk, p, seed).cpu().numpy().astype(bool)
+    ref = oracle.dropout_keep(seed, seq, head, np.arange(q0, q0 + nq)[:, None],
+                              np.arange(k0, k0 + nk)[None, :], oracle.dropout_threshold(p))
+    assert np.array_equal(got, ref)
+
+
+EDGE = [0, 1, 63, 64, 65, 127, 128, 129]
+
+# The backward's contractions take Z = P * keep / (1 - p) (dV) and dS (dK, dQ) as bf16
+# operands. On the edge workloads below - one sequence sums about 400 rounded weights near
+# 0.4 into every dV entry of its 3 keys - those roundings alone, applied to the oracle's
+# fp64 values, move 12 gradient elements beyond 2e-2 + 2e-2 |ref| and stay within 0.59 of
+# 6e-2 + 2e-2 |ref| (tests/test_tolerance_derivation.py, CPU). The edge backward is held to
+# that bound; outputs, LSE, the realisation and the full-size gradients to the standard ones.
+DROPOUT_GRAD_TOL = (6e-2, 2e-2)
+
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,window", [(1, 0), (2, 0), (0, 0), (2, 70)])
+def test_dropout_forward_edges(dtype, d, mode, window):
+    """Ragged lengths around the tile edges, GQA 4:2: O against the oracle with the same
+    realisation, LSE against the undropped oracle LSE."""
+    lq = EDGE + [5, 200]
+    lk = EDGE[::-1] + [300, 3]
+    w = wl.random_workload((41, d, mode), lq, lk, 4, 2, d, dtype, mode, window, name="drop-edge",
+                           v_offsets=True)
+    print(f"dropout fwd dtype={dtype} d={d} mode={mode} window={window}", flush=True)
+    t = to_device(w)
+    for p, seed in ((0.1, 7), (0.5, 2**40 + 3)):
+        out, lse = fwd_drop(w, t, p, seed)
+        ro, rl = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode, w.window,
+                                  dropout_p=p, seed=seed)
+        assert_close(to_np(out), ro, *tol_for(w), f"dropout O p={p}")
+        assert_close(to_np(lse), rl, LSE_TOL, 0.0, f"dropout LSE p={p}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,window", [(1, 0), (2, 0), (0, 0), (1, 70)])
+def test_dropout_backward_edges(d, mode, window):
+    """dQ, dK, dV (GQA group sums) against the oracle replaying the forward's realisation."""
+    lq = EDGE + [5, 200]
+    lk = EDGE[::-1] + [300, 3]
+    # N(0,1) values: the backward forms D = rowsum(dO * O) from the stored bf16 output, so
+    # the forward tests' large per-sequence value offsets would put its rounding (spacing
+    # 0.5 near |O| = 90) far above the gradient tolerance.
+    w = wl.random_workload((42, d, mode), lq, lk, 4, 2, d, "bf16", mode, window,
+                           with_dout=True, name="drop-bwd")
+    print(f"dropout bwd d={d} mode={mode} window={window}", flush=True)
+    t = to_device(w)
+    p, seed = 0.2, 99
+    out, lse = fwd_drop(w, t, p, seed)
+    got = bwd_drop(w, t, out, lse, p, seed)
+    ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
+                               w.window, dropout_p=p, seed=seed)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        worst = assert_close(to_np(g), r, *DROPOUT_GRAD_TOL, f"dropout {name}")
+        print(f"dropout {name}: {worst}", flush=True)
+
+
+def test_dropout_replays_across_packings():
+    """A sequence's dropout output and gradients are bitwise the same when the other
+    sequences of the pack change length (its storage offsets move; its index, heads and
+    positions do not)."""
+    a = wl.random_workload(43, [300, 0, 257, 5], [310, 3, 257, 9], 4, 2, 128, "bf16",
+                           wl.MASK_CAUSAL_TOP_LEFT, with_dout=True, name="pack-a")
+    b = wl.random_workload(44, [17, 129, 257, 64], [1, 200, 257, 64], 4, 2, 128, "bf16",
+                           wl.MASK_CAUSAL_TOP_LEFT, with_dout=True, name="pack-b")
+    qa, ka, qb, kb = int(a.cu_q[2]), int(a.cu_k[2]), int(b.cu_q[2]), int(b.cu_k[2])
+    for name in ("q", "dout"):
+        getattr(b, name)[qb:qb + 257] = getattr(a, name)[qa:qa + 257]
+    for name in ("k", "v"):
+        getattr(b, name)[kb:kb + 257] = getattr(a, name)[ka:ka + 257]
+    res = []
+    for w in (a, b):
+        t = to_device(w)
+        out, lse = fwd_drop(w, t, 0.3, 1234)
+        res.append((to_np(out), to_np(lse)) + tuple(to_np(x) for x in bwd_drop(w, t, out, lse,
+                                                                                0.3, 1234)))
+    (oa, la, dqa, dka, dva), (ob, lb, dqb, dkb, dvb) = res
+    assert np.array_equal(oa[qa:qa + 257], ob[qb:qb + 257])
+    assert np.array_equal(la[:, qa:qa + 257], lb[:, qb:qb + 257])
+    assert np.array_equal(dqa[qa:qa + 257], dqb[qb:qb + 257])
+    assert np.array_equal(dka[ka:ka + 257], dkb[kb:kb + 257])
+    assert np.array_equal(dva[ka:ka + 257], dvb[kb:kb + 257])
+
+
+def test_dropout_zero_probability_is_attn_fwd():
+    """p = 0 is the deterministic operator: attn_fwd_dropout then runs attn_fwd's kernels."""
+    import exact_attention_tiled_amd as eat
+    w = wl.random_workload(45, [200, 77], [200, 90], 4, 2, 128, "bf16",
+                           wl.MASK_CAUSAL_BOTTOM_RIGHT, name="p0")
+    t = to_device(w)
+    out, lse = fwd_drop(w, t, 0.0, 5)
+    out2, lse2 = eat.attn_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q,
+                              w.max_seqlen_k, w.scale, w.mask_mode, w.window,
+                              path=eat.ATTN_PATH_PREFILL)
+    assert np.array_equal(to_np(out), to_np(out2)) and np.array_equal(to_np(lse), to_np(lse2))
+
+
+def test_dropout_train_full_size():
+    """The training workload (B=2, Hq=32, Hkv=8, N=8192, d=128, top-left) with p = 0.1:
+    full GPU forward + backward; the oracle replays the realisation on one (sequence, K/V
+    head group): O and LSE of its 4 query heads, dQ, dK, dV of the group."""
+    w = wl.train_bf16()
+    t = to_device(w)
+    p, seed = 0.1, 2026
+    print("dropout train full size", flush=True)
+    out, lse = fwd_drop(w, t, p, seed)
+    dq, dk, dv = bwd_drop(w, t, out, lse, p, seed)
+    o, l, gq, gk, gv = (to_np(x) for x in (out, lse, dq, dk, dv))
+    for x in (o, l, gq, gk, gv):
+        assert np.all(np.isfinite(x))
+    s, g = 0, 5
+    heads = list(range(4 * g, 4 * g + 4))
+    ro, rl = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode, w.window,
+                              seqs=[s], heads=heads, dropout_p=p, seed=seed)
+    rq, rk, rv = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale,
+                                      w.mask_mode, w.window, seqs=[s], kv_heads=[g],
+                                      dropout_p=p, seed=seed)
+    rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+    assert_close(o[rows][:, heads], ro[rows][:, heads], *BF16_TOL, "dropout train O")
+    assert_close(l[heads][:, rows], rl[heads][:, rows], LSE_TOL, 0.0, "dropout train LSE")
+    assert_close(gq[rows][:, heads], rq[rows][:, heads], *BF16_TOL, "dropout train dQ")
+    assert_close(gk[rows][:, g], rk[rows][:, g], *BF16_TOL, "dropout train dK")
+    assert_close(gv[rows][:, g], rv[rows][:, g], *BF16_TOL, "dropout train dV")

@@ -195,3 +195,34 @@ def test_dropout_finite_differences():
     pins.check_finite_differences(
         lambda *a: oracle.attention(*a, **kw),
         lambda *a: oracle.attention_bwd(*a, **kw))
+
+
+def test_backward_from_a_given_output():
+    """``out=``: D is formed from the given output. With the oracle's own output the
+    gradients are unchanged; shifting one stored element O[t, h, m] by c shifts dQ[t, h] by
+    -scale c dO[t, h, m] sum_u P[t, u] k_u (the attention output with V = K), the keys' dK
+    summed over the sequence by -scale c dO[t, h, m] q[t, h] (the weights sum to 1), and
+    leaves dV unchanged (D does not enter it)."""
+    w = wl.random_workload(125, [6, 9], [7, 9], 4, 2, 8, "f32", wl.MASK_CAUSAL_BOTTOM_RIGHT,
+                           with_dout=True, name="given-out")
+    args = (w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode)
+    o, _ = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode)
+    base = oracle.attention_bwd(*args)
+    same = oracle.attention_bwd(*args, out=o)
+    for a, b in zip(base, same):
+        assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+    t, h, m, c = 8, 3, 5, 0.37        # token 8 is position 2 of sequence 1; K/V head 1
+    o2 = o.copy()
+    o2[t, h, m] += c
+    dq2, dk2, dv2 = oracle.attention_bwd(*args, out=o2)
+    g = h // 2
+    coef = -w.scale * c * float(np.asarray(w.dout, np.float64)[t, h, m])
+    ok_, _ = oracle.attention(w.q, w.k, w.k, w.cu_q, w.cu_k, w.scale, w.mask_mode)
+    assert np.allclose(dq2[t, h] - base[0][t, h], coef * ok_[t, h], rtol=1e-10, atol=1e-12)
+    others = np.ones(len(dq2), dtype=bool)
+    others[t] = False
+    assert np.allclose(dq2[others], base[0][others], rtol=0, atol=1e-14)
+    ka, kb = int(w.cu_k[1]), int(w.cu_k[2])
+    assert np.allclose((dk2 - base[1])[ka:kb, g].sum(axis=0),
+                       coef * np.asarray(w.q, np.float64)[t, h], rtol=1e-10, atol=1e-12)
+    assert np.array_equal(dv2, base[2])
