@@ -1,15 +1,16 @@
 """Benchmark of the exact tiled attention kernels on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|ragged|decode16|
-                    decode1|decode4|train|train_w1024] [--no-secondary] [--cpu-seconds S]
+                    decode1|decode4|train|train_w1024|train_drop] [--no-secondary] [--cpu-seconds S]
     python bench.py --sweep [--steps K] [--warmup W]    (sequence-length scaling and memory)
 
 Headline (one JSON line on stdout): the dense bf16 causal forward workload (B=4, Hq=Hkv=16,
 N=2048, d=128, causal top-left), reported as causal-adjusted TFLOP/s: 4 * d * (allowed
 query-key pairs over all heads) per forward, with inputs resident in HBM before timing.
 A "step" is one attn_fwd call (the whole forward path: tile scheduling, mask, QK^T, online
-softmax, PV, LSE). Secondary workloads (cached decode GB/s, training fwd+bwd TFLOP/s) are
-measured the same way and reported under "secondary".
+softmax, PV, LSE). Secondary workloads (cached decode GB/s, training fwd+bwd TFLOP/s, the
+same training step with dropout p = 0.1) are measured the same way and reported under
+"secondary".
 
 Protocol ("Attention Kernel Portability and Benchmarking", fourth and fifth sections):
 outputs are validated against the fp64 oracle on a sample before timing; warm-up calls;
@@ -164,10 +165,12 @@ def make_workload(name: str):
         return wl.train_bf16()
     if name == "train_w1024":
         return wl.train_bf16(window=1024)
+    if name == "train_drop":
+        return wl.train_bf16()
     raise ValueError(name)
 
 
-def validate_sample(w, out, lse, grads=None):
+def validate_sample(w, out, lse, grads=None, dropout=None):
     """Outputs checked against the oracle on one (sequence, head group) slice before any
     timing is interpreted ("Attention Kernel Portability and Benchmarking", fifth section)."""
     import oracle
@@ -175,8 +178,9 @@ def validate_sample(w, out, lse, grads=None):
     grp = w.hq // w.hkv
     heads = list(range(grp))
     rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+    dkw = {} if dropout is None else {"dropout_p": dropout[0], "seed": dropout[1]}
     ro, rl = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode, w.window,
-                              seqs=[s], heads=heads)
+                              seqs=[s], heads=heads, **dkw)
     o = out.double().cpu().numpy()[rows][:, heads]
     l = lse.double().cpu().numpy()[heads][:, rows]
     ok = np.all(np.abs(o - ro[rows][:, heads]) <= 2e-2 + 2e-2 * np.abs(ro[rows][:, heads]))
@@ -184,7 +188,7 @@ def validate_sample(w, out, lse, grads=None):
     ok &= np.all(np.abs(l[fin] - rl[heads][:, rows][fin]) <= 1e-3)
     if grads is not None:
         rq, rk, rv = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale,
-                                          w.mask_mode, w.window, seqs=[s], kv_heads=[0])
+                                          w.mask_mode, w.window, seqs=[s], kv_heads=[0], **dkw)
         krows = slice(int(w.cu_k[s]), int(w.cu_k[s + 1]))
         for g, r, sl, hs in ((grads[0], rq, rows, heads), (grads[1], rk, krows, [0]),
                              (grads[2], rv, krows, [0])):
@@ -224,7 +228,11 @@ def bench_forward(w, steps, warmup, validate=True):
     return {"wall_s": wall, "mean_ms": mean_ms, "ms": ms, "plan": plan, "validated": valid}
 
 
-def bench_train(w, steps, warmup, validate=True):
+# Dropout leg: probability and seed of the realisation (inverted dropout on the weights).
+TRAIN_DROPOUT = (0.1, 20261202)
+
+
+def bench_train(w, steps, warmup, validate=True, dropout=None):
     import torch
     import exact_attention_tiled_amd as eat
     dev = torch.device("cuda:0")
@@ -240,12 +248,22 @@ def bench_train(w, steps, warmup, validate=True):
     fws = torch.empty(1, dtype=torch.uint8, device=dev)
 
     def fwd():
-        eat.attn_fwd(q, k, v, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
-                     w.window, out=out, lse=lse, workspace=fws)
+        if dropout is None:
+            eat.attn_fwd(q, k, v, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale,
+                         w.mask_mode, w.window, out=out, lse=lse, workspace=fws)
+        else:
+            eat.attn_fwd_dropout(q, k, v, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale,
+                                 w.mask_mode, w.window, dropout[0], dropout[1], out=out,
+                                 lse=lse, workspace=fws)
 
     def bwd():
-        eat.attn_bwd(q, k, v, out, lse, do, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale,
-                     w.mask_mode, w.window, dq=dq, dk=dk, dv=dv, workspace=ws)
+        if dropout is None:
+            eat.attn_bwd(q, k, v, out, lse, do, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k,
+                         w.scale, w.mask_mode, w.window, dq=dq, dk=dk, dv=dv, workspace=ws)
+        else:
+            eat.attn_bwd_dropout(q, k, v, out, lse, do, cu_q, cu_k, w.max_seqlen_q,
+                                 w.max_seqlen_k, w.scale, w.mask_mode, w.window, dropout[0],
+                                 dropout[1], dq=dq, dk=dk, dv=dv, workspace=ws)
 
     def step():
         fwd()
@@ -253,7 +271,7 @@ def bench_train(w, steps, warmup, validate=True):
 
     step()
     torch.cuda.synchronize()
-    if validate and not validate_sample(w, out, lse, grads=(dq, dk, dv)):
+    if validate and not validate_sample(w, out, lse, grads=(dq, dk, dv), dropout=dropout):
         raise SystemExit(f"validation against the oracle failed for {w.name}; not timing it")
     # Peak memory of the timed calls only (validation makes float64 copies).
     torch.cuda.reset_peak_memory_stats()
@@ -418,7 +436,8 @@ def main():
                 "unit": "GB/s"}
         kernel = "fwd_splitk_kernel"
     elif args.workload.startswith("train"):
-        r = bench_train(w, args.steps, args.warmup)
+        r = bench_train(w, args.steps, args.warmup,
+                        dropout=TRAIN_DROPOUT if args.workload == "train_drop" else None)
         flops = 14.0 * w.d * pairs
         ms_avg = r["mean_ms"]
         value = flops * args.steps / r["wall_s"] / 1e12
@@ -453,7 +472,7 @@ def main():
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     if not args.no_secondary and args.workload == "dense":
         sec = []
-        for name in ("decode16", "train"):
+        for name in ("decode16", "train", "train_drop"):
             sw = make_workload(name)
             sp = allowed_pairs(sw)
             if name.startswith("decode"):
@@ -464,11 +483,13 @@ def main():
                             "frac_of_hbm_peak": b / (rr["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                             "step_stats": stats(rr["ms"])})
             else:
-                rr = bench_train(sw, 5, 2)
+                drop = TRAIN_DROPOUT if name == "train_drop" else None
+                rr = bench_train(sw, 5, 2, dropout=drop)
                 fwd_tf = 4.0 * sw.d * sp / (rr["mean_fwd"] * 1e-3) / 1e12
                 bwd_tf = 10.0 * sw.d * sp / (rr["mean_bwd"] * 1e-3) / 1e12
                 tot = 14.0 * sw.d * sp / (rr["mean_ms"] * 1e-3) / 1e12
-                sec.append({"workload": sw.name, "metric": "fwd+bwd TFLOP/s", "value": tot,
+                wname = sw.name if drop is None else f"{sw.name}_dropout{drop[0]}"
+                sec.append({"workload": wname, "metric": "fwd+bwd TFLOP/s", "value": tot,
                             "fwd_tflops": fwd_tf, "bwd_tflops": bwd_tf,
                             "frac_of_bf16_peak": tot / PEAK_BF16_TFLOPS,
                             "step_stats": stats(rr["ms"])})

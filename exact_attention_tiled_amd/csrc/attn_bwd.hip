@@ -262,10 +262,12 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
       }
       if constexpr (DROP) {
         const DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
+        // registers 4a..4a+3 hold queries qa + 8 a + 4 hg + 0..3 against key kj
+        uint32_t keeps[4];
+        dropout_keep_cols4(drop, (qa + 4 * hg) >> 2, kj, keeps);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          // registers 4a..4a+3 hold queries qa + 8 a + 4 hg + 0..3 against key kj
-          const uint32_t keep = dropout_keep_col(drop, (qa + 8 * a + 4 * hg) >> 2, kj);
+          const uint32_t keep = keeps[a];
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int r = 4 * a + b;
@@ -418,10 +420,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       M::qk(dpacc, vt + kb * 32 * ROWB, dor, of, lane);
       if constexpr (DROP) {
         const DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
+        // registers 4a..4a+3 hold keys k0 + 32 kb + 8 a + 4 hg + 0..3 against query pq
+        uint32_t keeps[4];
+        dropout_keep_rows4(drop, pq, (k0 + 32 * kb + 4 * hg) >> 2, keeps);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          // registers 4a..4a+3 hold keys k0 + 32 kb + 8 a + 4 hg + 0..3 against query pq
-          const uint32_t keep = dropout_keep_row(drop, pq, (k0 + 32 * kb + 8 * a + 4 * hg) >> 2);
+          const uint32_t keep = keeps[a];
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int r = 4 * a + b;

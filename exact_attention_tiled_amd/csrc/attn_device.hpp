@@ -278,6 +278,63 @@ __device__ __forceinline__ uint32_t dropout_keep_col(const DropoutSite& d, int q
   return bits;
 }
 
+// The 4 lanes of an aligned quad share a query quad (forward, dQ) or a key quad (dK/dV), so
+// the 4 patches a quad needs for the 4 register groups of a 32 x 32 block are computed
+// once each: lane c of the quad generates the patch of group c, and every lane fetches the
+// words it needs from the quad with DPP broadcasts (whole wave active).
+template <int A>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, A * 0x55, 0xF, 0xF, false);
+}
+
+// Row form: keep[a] bit b = key 4 (kp0 + 2 a) + b for this lane's query pq (pq & 3 equals
+// the lane's position in its quad). Group a covers keys 8 a + 4 (lane / 32) + 0..3 of a
+// 32-key block, so kp0 = (block start + 4 (lane / 32)) / 4.
+__device__ __forceinline__ void dropout_keep_rows4(const DropoutSite& d, int pq, int kp0,
+                                                   uint32_t (&keep)[4]) {
+  const int c = pq & 3;
+  uint32_t w[4];
+  dropout_patch(d, pq >> 2, kp0 + 2 * c, w);
+  uint32_t x[4][4];  // x[a][v] = word v of group a's patch
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    x[0][v] = quad_bcast<0>(w[v]);
+    x[1][v] = quad_bcast<1>(w[v]);
+    x[2][v] = quad_bcast<2>(w[v]);
+    x[3][v] = quad_bcast<3>(w[v]);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t y = (c & 2) ? ((c & 1) ? x[a][3] : x[a][2]) : ((c & 1) ? x[a][1] : x[a][0]);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bits |= (((y >> (8 * b)) & 0xFFu) >= d.thr ? 1u : 0u) << b;
+    keep[a] = bits;
+  }
+}
+
+// Column form: keep[a] bit v = query 4 (qp0 + 2 a) + v for this lane's key pk (pk & 3
+// equals the lane's position in its quad). Group a covers queries 8 a + 4 (lane / 32) + 0..3
+// of a 32-query block, so qp0 = (block start + 4 (lane / 32)) / 4.
+__device__ __forceinline__ void dropout_keep_cols4(const DropoutSite& d, int qp0, int pk,
+                                                   uint32_t (&keep)[4]) {
+  const int c = pk & 3;
+  uint32_t w[4];
+  dropout_patch(d, qp0 + 2 * c, pk >> 2, w);
+  const int sh = 8 * c;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) keep[a] = 0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint32_t x0 = quad_bcast<0>(w[v]), x1 = quad_bcast<1>(w[v]);
+    const uint32_t x2 = quad_bcast<2>(w[v]), x3 = quad_bcast<3>(w[v]);
+    keep[0] |= (((x0 >> sh) & 0xFFu) >= d.thr ? 1u : 0u) << v;
+    keep[1] |= (((x1 >> sh) & 0xFFu) >= d.thr ? 1u : 0u) << v;
+    keep[2] |= (((x2 >> sh) & 0xFFu) >= d.thr ? 1u : 0u) << v;
+    keep[3] |= (((x3 >> sh) & 0xFFu) >= d.thr ? 1u : 0u) << v;
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Swizzled LDS tiles filled by buffer -> LDS DMA.
 //

@@ -104,14 +104,14 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack 
 #pragma unroll
       for (int r = 0; r < 16; ++r) sum += s[kb][r];
       l_run += sum;
+      // registers 4a..4a+3 hold keys kpos0 + 32 kb + 8 a + 4 hg + 0..3
+      uint32_t keep[4];
+      dropout_keep_rows4(drop, pq, (kpos0 + 32 * kb + 4 * hg) >> 2, keep);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        // registers 4a..4a+3 hold keys kpos0 + 32 kb + 8 a + 4 hg + 0..3
-        const uint32_t keep = dropout_keep_row(drop, pq, (kpos0 + 32 * kb + 8 * a + 4 * hg) >> 2);
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          s[kb][4 * a + b] = ((keep >> b) & 1u) ? s[kb][4 * a + b] * drop.scale : 0.0f;
-      }
+          s[kb][4 * a + b] = ((keep[a] >> b) & 1u) ? s[kb][4 * a + b] * drop.scale : 0.0f;
       (void)M::pack_p(s[kb], pk[kb]);
     }
   } else {
