@@ -169,3 +169,48 @@ def test_dropout_train_full_size():
     assert_close(gq[rows][:, heads], rq[rows][:, heads], *BF16_TOL, "dropout train dQ")
     assert_close(gk[rows][:, g], rk[rows][:, g], *BF16_TOL, "dropout train dK")
     assert_close(gv[rows][:, g], rv[rows][:, g], *BF16_TOL, "dropout train dV")
+
+
+def test_dropout_canaries_no_out_of_bounds_writes():
+    """The dropout forward and backward write only inside their outputs: O, LSE, dQ, dK, dV
+    land inside larger buffers whose slack holds sentinels, and every sentinel survives.
+    Keys no query can see get exactly zero dK/dV, whatever the realisation."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    lq, lk = [40, 3, 90], [10, 200, 90]
+    w = wl.random_workload(46, lq, lk, 4, 1, 64, "bf16", wl.MASK_CAUSAL_BOTTOM_RIGHT, 16,
+                           with_dout=True, name="drop-canary")
+    t = to_device(w)
+    pad, sentinel = 4096, -12345.0
+
+    def padded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * pad,), sentinel, dtype=dtype, device="cuda")
+        return buf, buf[pad:pad + n].view(shape)
+
+    bo, out = padded(t["q"].shape, t["q"].dtype)
+    bl, lse = padded((w.hq, w.total_q), torch.float32)
+    eat.attn_fwd_dropout(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q,
+                         w.max_seqlen_k, w.scale, w.mask_mode, w.window, 0.25, 777, out=out,
+                         lse=lse)
+    bq, dq = padded(t["q"].shape, t["q"].dtype)
+    bk, dk = padded(t["k"].shape, t["k"].dtype)
+    bv, dv = padded(t["v"].shape, t["v"].dtype)
+    eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out, lse, t["dout"], t["cu_q"], t["cu_k"],
+                         w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode, w.window, 0.25,
+                         777, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for buf in (bo, bl, bq, bk, bv):
+        assert torch.all(buf[:pad] == sentinel) and torch.all(buf[-pad:] == sentinel)
+    m = oracle.explicit_mask(w.cu_q, w.cu_k, w.mask_mode, w.window)
+    unseen = torch.from_numpy(np.nonzero(~m.any(axis=0))[0]).cuda()
+    assert len(unseen) > 50
+    assert torch.all(dk[unseen].float() == 0) and torch.all(dv[unseen].float() == 0)
+    ro, rl = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode, w.window,
+                              dropout_p=0.25, seed=777)
+    assert_close(to_np(out), ro, *BF16_TOL, "dropout canary O")
+    assert_close(to_np(lse), rl, LSE_TOL, 0.0, "dropout canary LSE")
+    ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
+                               w.window, dropout_p=0.25, seed=777)
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        assert_close(to_np(g), r, *DROPOUT_GRAD_TOL, f"dropout canary {name}")
