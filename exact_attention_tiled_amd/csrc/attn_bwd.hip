@@ -1,8 +1,8 @@
 // attn_bwd.hip - backward kernels: preprocess, main (dK, dV and dQ contributions), dQ convert.
 //
-// The backward rebuilds P from the saved log-sum-exp instead of storing it, with the same
-// mask unit as the forward ("Causal Mask and Ragged Sequence Layouts", sixth section:
-// backward recomputation must rebuild the same logical mask), and sums the K/V gradients
+// The backward rebuilds P from the saved log-sum-exp instead of storing it, deciding which
+// pairs count with the forward's own interval rules, so that its mask is the forward's
+// ("Causal Mask and Ragged Sequence Layouts", sixth section), and sums the K/V gradients
 // over each GQA group ("Attention Algorithm Error and Complexity Tests", third section).
 // Per (query, key) pair, with c = scale * log2(e):
 //   P   = exp2(c S - LSE log2 e)  (0 for disallowed pairs and out-of-range lanes)
@@ -583,7 +583,7 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, void* ws, hipStream_t st) {
-  if (a.f.dtype != 0) return hipErrorNotSupported;
+  if (a.f.dtype != 0) return hipErrorNotSupported;  // the ABI rejects fp32 before this point
   return a.f.d == 64 ? bwd_typed<64>(a, ws, st) : bwd_typed<128>(a, ws, st);
 }
 

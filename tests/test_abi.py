@@ -97,6 +97,18 @@ def test_bwd_validation(lib):
     assert need >= 2 * 4 * 2 * 4   # D and LSE (base 2) per (query, head), fp32
 
 
+def test_bwd_rejects_f32_on_the_host(lib):
+    """The backward kernels are bf16 only: fp32 is a validation error returned before any
+    launch (no device is needed to see it), and the size query answers 0 for it."""
+    args = [1] * 8 + [1, 4, 4, 4, 4, 2, 1, 64, 1, ctypes.c_float(0.1), 1, 0, 1, 1, 1, 1, 1 << 20,
+                      None]
+    assert lib.attn_bwd(*args) == BAD_DTYPE
+    dargs = args[:20] + [ctypes.c_float(0.1), ctypes.c_uint64(5)] + args[20:]
+    assert lib.attn_bwd_dropout(*dargs) == BAD_DTYPE
+    assert lib.attn_bwd_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 1, 1, 0) == 0
+    assert lib.attn_bwd_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 0, 1, 0) > 0
+
+
 def test_mask_probe_validation(lib):
     assert lib.attn_mask_probe(1, 1, 1, 4, 4, 1, 0, 0, 5, 0, 4, 1, None) == BAD_RANGE
     assert lib.attn_mask_probe(1, 1, 1, 4, 4, 0, 3, 0, 4, 0, 4, 1, None) == BAD_MASK

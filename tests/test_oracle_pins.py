@@ -17,18 +17,33 @@ def obwd(q, k, v, do, cu_q, cu_k, scale, mode, window):
     return oracle.attention_bwd(q, k, v, do, cu_q, cu_k, scale, mode, window)
 
 
+def ofwd_explicit(q, k, v, cu_q, cu_k, scale, mode, window):
+    return oracle.attention_explicit(q, k, v, oracle.explicit_mask(cu_q, cu_k, mode, window),
+                                     scale)
+
+
+def obwd_explicit(q, k, v, do, cu_q, cu_k, scale, mode, window):
+    """The explicit-mask backward over the whole pack (one [Tq, Tk] mask for every head),
+    fed the mask that sequence ids and positions give."""
+    return oracle.attention_explicit_bwd(q, k, v, do,
+                                         oracle.explicit_mask(cu_q, cu_k, mode, window), scale)
+
+
 @pytest.mark.parametrize("check", pins.FWD_CHECKS, ids=lambda f: f.__name__)
 def test_oracle_forward_pins(check):
     check(ofwd)
 
 
 @pytest.mark.parametrize("check", pins.BWD_CHECKS, ids=lambda f: f.__name__)
-def test_oracle_backward_pins(check):
-    check(obwd)
+@pytest.mark.parametrize("bwd", [obwd, obwd_explicit], ids=["per_sequence", "explicit_mask"])
+def test_oracle_backward_pins(check, bwd):
+    check(bwd)
 
 
-def test_oracle_finite_differences():
-    pins.check_finite_differences(ofwd, obwd)
+@pytest.mark.parametrize("fwd,bwd", [(ofwd, obwd), (ofwd_explicit, obwd_explicit)],
+                         ids=["per_sequence", "explicit_mask"])
+def test_oracle_finite_differences(fwd, bwd):
+    pins.check_finite_differences(fwd, bwd)
 
 
 def test_explicit_mask_matches_golden():
@@ -113,6 +128,25 @@ def test_causal_permutation_with_explicit_mask():
     pins._close(lse2, lse, 1e-13, "LSE")
     o3, _ = oracle.attention_explicit(q, k[perm], v[perm], m, 0.7)
     assert np.abs(o3 - o).max() > 1e-3   # permuting without the mask changes the operator
+
+
+def test_causal_permutation_backward_with_explicit_mask():
+    """The same consistent permutation of keys, values and mask columns leaves dQ unchanged
+    and permutes dK and dV the same way (the backward rebuilds the permuted mask: "Causal
+    Mask and Ragged Sequence Layouts", sixth section)."""
+    rng = np.random.default_rng(19)
+    q, k, v, cu_q, cu_k = pins._random_pack(rng, [6], [8], 4, 2, 3)
+    do = rng.standard_normal(q.shape)
+    for mode, window in ((2, 0), (1, 3)):
+        m = oracle.explicit_mask(cu_q, cu_k, mode, window)
+        dq, dk, dv = oracle.attention_explicit_bwd(q, k, v, do, m, 0.7)
+        perm = rng.permutation(8)
+        dq2, dk2, dv2 = oracle.attention_explicit_bwd(q, k[perm], v[perm], do, m[:, perm], 0.7)
+        pins._close(dq2, dq, 1e-13, "permuted dQ")
+        pins._close(dk2, dk[perm], 1e-13, "permuted dK")
+        pins._close(dv2, dv[perm], 1e-13, "permuted dV")
+        dq3, _, _ = oracle.attention_explicit_bwd(q, k[perm], v[perm], do, m, 0.7)
+        assert np.abs(dq3 - dq).max() > 1e-3   # without the mask columns it is another operator
 
 
 def test_split_key_ranges_combine_to_full():
