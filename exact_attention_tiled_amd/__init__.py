@@ -7,5 +7,5 @@ from ._binding import (  # noqa: F401
     ATTN_BF16, ATTN_F32, ATTN_MASK_NONE, ATTN_MASK_CAUSAL_TOP_LEFT, ATTN_MASK_CAUSAL_BOTTOM_RIGHT,
     ATTN_PATH_AUTO, ATTN_PATH_PREFILL, ATTN_PATH_SPLITK, EXPORTS, AttnError, attn_bwd,
     attn_bwd_dropout, attn_bwd_workspace_size, attn_describe_plan, attn_dropout_probe, attn_fwd,
-    attn_fwd_dropout, attn_fwd_workspace_size, attn_mask_probe, attn_status_string,
-    attn_version, library_path, load)
+    attn_fwd_dropout, attn_fwd_no_workspace, attn_fwd_workspace_size, attn_mask_probe,
+    attn_status_string, attn_version, library_path, load)

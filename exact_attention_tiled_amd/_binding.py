@@ -22,7 +22,8 @@ ATTN_PATH_AUTO, ATTN_PATH_PREFILL, ATTN_PATH_SPLITK = 0, 1, 2
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_ex_workspace_size",
            "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_dropout",
            "attn_fwd_dropout_workspace_size", "attn_bwd_dropout", "attn_dropout_probe",
-           "attn_mask_probe", "attn_describe_plan", "attn_status_string", "attn_version")
+           "attn_mask_probe", "attn_describe_plan", "attn_status_string", "attn_version",
+           "attn_fwd_no_workspace")
 
 _lib = None
 
@@ -58,6 +59,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_ex.argtypes = [_P, _P, _P, _P, _P] + [_I] * 9 + [_F, _I, _I, _I, _I,
                                                                   _P, _P, _P, _S, _P]
     lib.attn_fwd_ex.restype = ctypes.c_int
+    lib.attn_fwd_no_workspace.argtypes = [_P, _P, _P, _P, _P] + [_I] * 9 + [_F, _I, _I, _P, _P, _P]
+    lib.attn_fwd_no_workspace.restype = ctypes.c_int
     lib.attn_fwd_workspace_size.argtypes = [_I] * 11
     lib.attn_fwd_workspace_size.restype = _S
     lib.attn_fwd_ex_workspace_size.argtypes = [_I] * 13
@@ -179,6 +182,25 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: to
                             _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream())
     _check("attn_fwd", rc)
     return out, lse
+
+
+def attn_fwd_no_workspace(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                          max_seqlen_q: int, max_seqlen_k: int, scale: float, mask_mode: int,
+                          window: int = 0, *, out: torch.Tensor, lse: torch.Tensor) -> None:
+    """attn_fwd without a workspace: the library's fixed device scratch stands in for it.
+    The caller passes the outputs (nothing is allocated here either)."""
+    _dev(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    n, tq, tk, mq, mk, hq, hkv, d = _shape_args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k)
+    rc = load().attn_fwd_no_workspace(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                      _ptr(cu_seqlens_k), n, tq, tk, mq, mk, hq, hkv, d,
+                                      _dtype_code(q), float(scale), int(mask_mode), int(window),
+                                      _ptr(out), _ptr(lse), _stream())
+    _check("attn_fwd_no_workspace", rc)
 
 
 def attn_bwd_workspace_size(q, k, cu_q, max_seqlen_q, max_seqlen_k, mask_mode, window=0) -> int:

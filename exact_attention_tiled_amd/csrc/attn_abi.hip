@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "attn_internal.h"
@@ -181,6 +182,31 @@ bool dropout_threshold(float p, uint32_t* thr, float* scale) {
   return true;
 }
 
+// Fixed device scratch of attn_fwd_no_workspace, for callers that cannot allocate (code
+// under graph capture, serving loops). Every GPU the library runs on holds its own copy
+// of this array until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is ever handed to kernels.
+static __device__ __align__(256) char scratch[ATTN_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch` per device (null until looked up)
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_UNSUPPORTED_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return ATTN_ERR_LAUNCH_FAILED;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +228,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_BAD_PLAN: return "forced path or split count not usable for this shape";
     case ATTN_ERR_BAD_RANGE: return "probe window outside the token ranges";
     case ATTN_ERR_BAD_DROPOUT: return "dropout probability not in [0, 255.5/256)";
+    case ATTN_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more scratch than the library's fixed 16 MiB (use attn_fwd)";
     default: return "unknown status";
   }
 }
@@ -264,6 +292,32 @@ int attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_q, c
   return attn_fwd_ex(q, k, v, cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d,
                      dtype, scale, mode, window, ATTN_PATH_AUTO, 0, out, lse, workspace,
                      workspace_bytes, stream);
+}
+
+int attn_fwd_no_workspace(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                          const int32_t* cu_k, int32_t num_seqs, int32_t total_q,
+                          int32_t total_k, int32_t max_q, int32_t max_k, int32_t hq,
+                          int32_t hkv, int32_t d, int32_t dtype, float scale, int32_t mode,
+                          int32_t window, void* out, float* lse, void* stream) {
+  // The same validation and plan as attn_fwd, in the same order, so errors match it.
+  int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                           window);
+  if (rc != ATTN_OK) return rc;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  Plan plan;
+  rc = make_plan(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, ATTN_PATH_AUTO, 0,
+                 planning_cu_count(), &plan);
+  if (rc != ATTN_OK) return rc;
+  if (plan.workspace > (size_t)ATTN_SCRATCH_BYTES) return ATTN_ERR_SCRATCH_TOO_SMALL;
+  if (num_seqs == 0 || total_q == 0) return ATTN_OK;
+  rc = check_device();
+  if (rc != ATTN_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != ATTN_OK) return rc;
+  return attn_fwd_ex(q, k, v, cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d,
+                     dtype, scale, mode, window, ATTN_PATH_AUTO, 0, out, lse, ws,
+                     (size_t)ATTN_SCRATCH_BYTES, stream);
 }
 
 size_t attn_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,

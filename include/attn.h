@@ -68,7 +68,8 @@ typedef enum attn_status {
   ATTN_ERR_BAD_SCALE = -9,            /* scale is not finite */
   ATTN_ERR_BAD_PLAN = -10,            /* forced path / split count not usable for the shape */
   ATTN_ERR_BAD_RANGE = -11,           /* probe window outside the token ranges */
-  ATTN_ERR_BAD_DROPOUT = -12          /* dropout probability not in [0, 255.5/256) */
+  ATTN_ERR_BAD_DROPOUT = -12,         /* dropout probability not in [0, 255.5/256) */
+  ATTN_ERR_SCRATCH_TOO_SMALL = -13    /* attn_fwd_no_workspace: needs more than the scratch */
 } attn_status;
 
 enum attn_dtype { ATTN_BF16 = 0, ATTN_F32 = 1 };
@@ -114,6 +115,31 @@ size_t attn_fwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_
                                int32_t max_seqlen_q, int32_t max_seqlen_k,
                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                                int32_t dtype, int32_t mask_mode, int32_t window);
+
+/*
+ * attn_fwd_no_workspace - attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Instead of a caller workspace it uses a fixed scratch array of
+ * ATTN_SCRATCH_BYTES that the library holds in device memory, one per GPU, until the
+ * process ends; it calls no allocator (no hipMalloc, hipFree or allocating library routine).
+ * Same arguments, plan, kernels and results as attn_fwd with ATTN_PATH_AUTO.
+ *   Limit: a call whose plan needs more than ATTN_SCRATCH_BYTES of workspace (what
+ *          attn_fwd_workspace_size reports for it) returns ATTN_ERR_SCRATCH_TOO_SMALL before
+ *          any launch; e.g. the split-K decode of 16 sequences x 32 query heads x 16 queries
+ *          at head_dim 128 needs about 8.4 MiB.
+ *   Concurrency: every call on one GPU shares that GPU's scratch, which keeps whatever the
+ *          last call left there. Calls that overlap in time on one GPU (other streams, other
+ *          threads) race on it; serialise them, or use attn_fwd with separate workspaces.
+ */
+#define ATTN_SCRATCH_BYTES (16u << 20)
+
+int attn_fwd_no_workspace(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int32_t num_seqs, int32_t total_q, int32_t total_k,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                          int32_t dtype, float scale, int32_t mask_mode, int32_t window,
+                          void* out, float* lse, void* stream);
 
 /*
  * attn_fwd_ex / attn_fwd_ex_workspace_size - the forward pass with the path chosen by the

@@ -12,7 +12,7 @@ from exact_attention_tiled_amd import build as eat_build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 OK, NULL_PTR, BAD_SHAPE, BAD_HEADS, BAD_DTYPE, BAD_MASK, WS_SMALL = 0, -1, -2, -3, -4, -5, -6
-BAD_SCALE, BAD_PLAN, BAD_RANGE, BAD_DROPOUT = -9, -10, -11, -12
+BAD_SCALE, BAD_PLAN, BAD_RANGE, BAD_DROPOUT, SCRATCH_SMALL = -9, -10, -11, -12, -13
 
 
 @pytest.fixture(scope="module")
@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_status_strings(lib):
     assert eat.attn_version() == 100
     for code in (OK, NULL_PTR, BAD_SHAPE, BAD_HEADS, BAD_DTYPE, BAD_MASK, WS_SMALL, -7, -8,
-                 BAD_SCALE, BAD_PLAN, BAD_RANGE, BAD_DROPOUT):
+                 BAD_SCALE, BAD_PLAN, BAD_RANGE, BAD_DROPOUT, SCRATCH_SMALL):
         s = eat.attn_status_string(code)
         assert s and s != "unknown status"
     assert eat.attn_status_string(12345) == "unknown status"
@@ -160,3 +160,28 @@ def test_dropout_validation(lib):
     assert lib.attn_dropout_probe(0, 0, 0, 4, 0, 4, f(1.0), 1, None, None) == BAD_DROPOUT
     assert lib.attn_dropout_probe(0, 0, 0, 0, 0, 4, f(0.1), 1, None, None) == OK
     assert lib.attn_dropout_probe(0, 0, 0, 4, 0, 4, f(0.1), 1, None, None) == NULL_PTR
+
+
+def test_no_workspace_validation(lib):
+    """attn_fwd_no_workspace validates like attn_fwd and refuses, before any launch, a plan
+    whose workspace exceeds the fixed scratch (host only: these calls never reach a GPU)."""
+    base = [1] * 5 + [1, 4, 4, 4, 4, 2, 1, 64, 0, ctypes.c_float(0.125), 1, 0, 1, 1, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return lib.attn_fwd_no_workspace(*a)
+
+    assert call(a12=96) == BAD_SHAPE
+    assert call(a10=3, a11=2) == BAD_HEADS
+    assert call(a13=7) == BAD_DTYPE
+    assert call(a15=0, a16=5) == BAD_MASK
+    assert call(a14=ctypes.c_float(float("inf"))) == BAD_SCALE
+    # split-K decode of 64 sequences x 64 query heads x 8 queries against 64k keys: the
+    # partials need far more than the scratch
+    big = dict(a5=64, a6=64 * 8, a7=64 * 65536, a8=8, a9=65536, a10=64, a11=8, a12=128, a15=2)
+    need = lib.attn_fwd_workspace_size(64, 64 * 8, 64 * 65536, 8, 65536, 64, 8, 128, 0, 2, 0)
+    assert need > (16 << 20)
+    assert call(**big) == SCRATCH_SMALL
+    assert call(a5=0) == OK           # empty batch: nothing to do
