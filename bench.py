@@ -245,7 +245,11 @@ def bench_train(w, steps, warmup, validate=True, dropout=None):
     wsb = eat.attn_bwd_workspace_size(q, k, cu_q, w.max_seqlen_q, w.max_seqlen_k, w.mask_mode,
                                       w.window)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    fws = torch.empty(1, dtype=torch.uint8, device=dev)
+    fwsb = (eat.attn_fwd_workspace_size(q, k, cu_q, w.max_seqlen_q, w.max_seqlen_k, w.mask_mode,
+                                        w.window) if dropout is None else
+            eat.attn_fwd_dropout_workspace_size(q, k, cu_q, w.max_seqlen_q, w.max_seqlen_k,
+                                                w.mask_mode, w.window))
+    fws = torch.empty(max(fwsb, 1), dtype=torch.uint8, device=dev)
 
     def fwd():
         if dropout is None:

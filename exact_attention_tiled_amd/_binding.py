@@ -18,12 +18,14 @@ LIB_PATH = os.path.join(_PKG, "lib", "libattn.so")
 ATTN_BF16, ATTN_F32 = 0, 1
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL_TOP_LEFT, ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 ATTN_PATH_AUTO, ATTN_PATH_PREFILL, ATTN_PATH_SPLITK = 0, 1, 2
+(ATTN_PROBE_PREFILL, ATTN_PROBE_PREFILL_GENERIC, ATTN_PROBE_SPLITK, ATTN_PROBE_BWD_KV,
+ ATTN_PROBE_BWD_Q) = 0, 1, 2, 3, 4
 
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_ex_workspace_size",
            "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_dropout",
            "attn_fwd_dropout_workspace_size", "attn_bwd_dropout", "attn_dropout_probe",
            "attn_mask_probe", "attn_describe_plan", "attn_status_string", "attn_version",
-           "attn_fwd_no_workspace")
+           "attn_fwd_no_workspace", "attn_mask_probe_ex")
 
 _lib = None
 
@@ -82,6 +84,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_dropout_probe.restype = ctypes.c_int
     lib.attn_mask_probe.argtypes = [_P, _P] + [_I] * 9 + [_P, _P]
     lib.attn_mask_probe.restype = ctypes.c_int
+    lib.attn_mask_probe_ex.argtypes = [_P, _P] + [_I] * 16 + [_P, _P]
+    lib.attn_mask_probe_ex.restype = ctypes.c_int
     lib.attn_describe_plan.argtypes = shape10 + [_I, _I, _I, ctypes.c_char_p, _S]
     lib.attn_describe_plan.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -91,6 +95,25 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     if path is None:
         _lib = lib
     return lib
+
+
+class use_library:
+    """Context manager: the binding's calls go to another build of the library (the race-
+    exposure build lib/libattn_poison.so, for tests) while it is active."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = load()
+        _lib = load(self.path)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def attn_status_string(status: int) -> str:
@@ -229,6 +252,14 @@ def attn_bwd(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
     return dq, dk, dv
 
 
+def attn_fwd_dropout_workspace_size(q, k, cu_q, max_seqlen_q, max_seqlen_k, mask_mode,
+                                    window=0) -> int:
+    n, tq, tk, mq, mk, hq, hkv, d = _shape_args(q, k, cu_q, max_seqlen_q, max_seqlen_k)
+    return int(load().attn_fwd_dropout_workspace_size(n, tq, tk, mq, mk, hq, hkv, d,
+                                                      _dtype_code(q), int(mask_mode),
+                                                      int(window)))
+
+
 def attn_fwd_dropout(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
                      mask_mode, window, dropout_p, seed, *, out=None, lse=None, workspace=None):
     """Forward with dropout on the attention weights (attn_fwd_dropout in include/attn.h):
@@ -300,4 +331,21 @@ def attn_mask_probe(cu_seqlens_q, cu_seqlens_k, total_q, total_k, mask_mode, win
                                 int(mask_mode), int(window), int(q0), int(nq), int(k0), int(nk),
                                 _ptr(bits), _stream())
     _check("attn_mask_probe", rc)
+    return bits
+
+
+def attn_mask_probe_ex(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                       num_heads_q, num_heads_kv, mask_mode, window, unit, q0, nq, k0, nk, *,
+                       head=0, num_splits=0) -> torch.Tensor:
+    """uint8 [nq, nk]: 1 where kernel unit `unit` (ATTN_PROBE_*) lets pair (q0+i, k0+j) into
+    its softmax (forward) or gradient sums (backward)."""
+    _dev(cu_seqlens_q, cu_seqlens_k)
+    bits = torch.empty((nq, nk), dtype=torch.uint8, device=cu_seqlens_q.device)
+    rc = load().attn_mask_probe_ex(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                   int(cu_seqlens_q.shape[0]) - 1, int(total_q), int(total_k),
+                                   int(max_seqlen_q), int(max_seqlen_k), int(num_heads_q),
+                                   int(num_heads_kv), int(mask_mode), int(window), int(unit),
+                                   int(head), int(num_splits), int(q0), int(nq), int(k0),
+                                   int(nk), _ptr(bits), _stream())
+    _check("attn_mask_probe_ex", rc)
     return bits

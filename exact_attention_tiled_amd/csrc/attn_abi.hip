@@ -360,23 +360,61 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
 }
 
-int attn_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs, int32_t total_q,
-                    int32_t total_k, int32_t mode, int32_t window, int32_t q0, int32_t nq,
-                    int32_t k0, int32_t nk, uint8_t* bits, void* stream) {
+int attn_mask_probe_ex(const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs,
+                       int32_t total_q, int32_t total_k, int32_t max_q, int32_t max_k,
+                       int32_t hq, int32_t hkv, int32_t mode, int32_t window, int32_t unit,
+                       int32_t head, int32_t num_splits, int32_t q0, int32_t nq, int32_t k0,
+                       int32_t nk, uint8_t* bits, void* stream) {
   if (num_seqs < 0 || total_q < 0 || total_k < 0) return ATTN_ERR_BAD_SHAPE;
   if (mode != ATTN_MASK_NONE && mode != ATTN_MASK_CAUSAL_TOP_LEFT &&
       mode != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
     return ATTN_ERR_BAD_MASK;
   if (window > 0 && mode == ATTN_MASK_NONE) return ATTN_ERR_BAD_MASK;
+  if (unit < ATTN_PROBE_PREFILL || unit > ATTN_PROBE_BWD_Q) return ATTN_ERR_BAD_PLAN;
   if (q0 < 0 || nq < 0 || k0 < 0 || nk < 0 || (long)q0 + nq > total_q || (long)k0 + nk > total_k)
     return ATTN_ERR_BAD_RANGE;
+  attn::ProbeArgs a{};
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.num_seqs = num_seqs;
+  a.mode = mode;
+  a.window = window > 0 ? window : 0;
+  a.unit = unit;
+  a.q0 = q0;
+  a.nq = nq;
+  a.k0 = k0;
+  a.nk = nk;
+  if (unit == ATTN_PROBE_SPLITK) {
+    // The split-K plan attn_fwd_ex would run for these shapes (bf16, head_dim 128).
+    int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, 128, ATTN_BF16,
+                             mode, window);
+    if (rc != ATTN_OK) return rc;
+    if (head < 0 || head >= hq) return ATTN_ERR_BAD_RANGE;
+    Plan plan;
+    rc = make_plan(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, 128, ATTN_BF16,
+                   ATTN_PATH_SPLITK, num_splits, planning_cu_count(), &plan);
+    if (rc != ATTN_OK) return rc;
+    a.group = hq / hkv;
+    a.head = head;
+    a.nsb = plan.nsb;
+    a.chunk = plan.chunk;
+    a.nrb = (long)a.group * max_q <= 32 ? 1 : 2;
+  }
   if (nq == 0 || nk == 0 || num_seqs == 0) return ATTN_OK;
   if (!cu_q || !cu_k || !bits) return ATTN_ERR_NULL_PTR;
   int rc = check_device();
   if (rc != ATTN_OK) return rc;
-  hipError_t e = attn::launch_mask_probe(cu_q, cu_k, num_seqs, mode, window > 0 ? window : 0, q0,
-                                         nq, k0, nk, bits, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = unit <= ATTN_PROBE_SPLITK ? attn::launch_mask_probe_fwd(a, bits, st)
+                                           : attn::launch_mask_probe_bwd(a, bits, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
+}
+
+int attn_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs, int32_t total_q,
+                    int32_t total_k, int32_t mode, int32_t window, int32_t q0, int32_t nq,
+                    int32_t k0, int32_t nk, uint8_t* bits, void* stream) {
+  return attn_mask_probe_ex(cu_q, cu_k, num_seqs, total_q, total_k, 0, 0, 1, 1, mode, window,
+                            ATTN_PROBE_PREFILL, 0, 0, q0, nq, k0, nk, bits, stream);
 }
 
 size_t attn_fwd_dropout_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k,

@@ -221,7 +221,14 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
     tile_of(it, h, q0);
     const int qend = min(q0 + BWD_BM, g.len_q);
     (void)h;
-    if (it + 1 < niter) issue_tile(it + 1, b ^ 1, nl2, ndv);
+    if (it + 1 < niter) {
+      if (tid < BWD_BM) {  // (race-exposure builds only) the slots this thread refills below
+        poison4(vecs + (b ^ 1) * 2 * BWD_BM + tid);
+        poison4(vecs + (b ^ 1) * 2 * BWD_BM + BWD_BM + tid);
+        poison_done();
+      }
+      issue_tile(it + 1, b ^ 1, nl2, ndv);
+    }
     const char* qtb = lds + L::Q_OFF + b * L::QT;
     const char* dotb = lds + L::DO_OFF + b * L::QT;
     const float* lse2s = vecs + b * 2 * BWD_BM;
@@ -232,8 +239,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
     if (cls != 0) {
       // Register r holds query position qa + key_of_reg(r, l / 32): allowed iff it lies in
       // this lane's key's query interval, one unsigned compare (every pair when cls == 2).
-      const unsigned qbase = (unsigned)(qa + 4 * hg - kq_lo);
-      const unsigned qwidth = cls == 2 ? 0xffffffffu : kq_width;
+      const KeyLaneTest allowed(qa, cls, hg, kq_lo, kq_width);
       typename M::PPack pp[1], pd[1];
       // S and dP with keys on the lanes: A = Q / dO rows, B = K / V rows (all from LDS).
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int r = 4 * a + b;
-            const bool ok = qbase + (unsigned)(8 * a + b) < qwidth;
+            const bool ok = allowed.ok(r);
             const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[a][b]));
             const float pv = ok ? e : 0.0f;
             const bool kept = (keep >> b) & 1u;
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool ok = qbase + (unsigned)(8 * (r >> 2) + (r & 3)) < qwidth;
+          const bool ok = allowed.ok(r);
           const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[r >> 2][r & 3]));
           const float pv = ok ? e : 0.0f;
           sacc[r] = pv;
@@ -390,10 +396,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   float dsum = 0.0f;  // DONLY: this lane's part of sum_j P dP
   const typename M::Offsets of = M::offsets(lane);
 
-  int klo, khi;
-  visible_keys(p0, p1, g, p.mode, p.window, klo, khi);
-  const int kstart = (klo / BN) * BN;
-  const int nst = khi > klo ? (khi - kstart + BN - 1) / BN : 0;
+  int kstart, nst;
+  stage_range(p0, p1, g, p.mode, p.window, BN, kstart, nst);
 
   const uint32_t rstride = (uint32_t)(p.hkv * D * 2);
   const char* kg = reinterpret_cast<const char*>(p.k + ((size_t)g.k_start * p.hkv + kvh) * D);
@@ -411,8 +415,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   auto stage = [&](const char* kt, const char* vt, int k0) {
     const int cls = block_class(wp0, wp1, k0, k0 + BN, g, p.mode, p.window);
     if (cls == 0) return;
-    const unsigned kbase = (unsigned)(k0 + 4 * hg - kv_lo);
-    const unsigned kwidth = cls == 2 ? 0xffffffffu : kv_width;
+    const QueryLaneTest allowed(k0, cls, hg, kv_lo, kv_width);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -429,7 +432,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int r = 4 * a + b;
-            const bool ok = kbase + (unsigned)(32 * kb + 8 * a + b) < kwidth;
+            const bool ok = allowed.ok(kb, r);
             const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));
             const float pv = ok ? e : 0.0f;
             const float dpz = ((keep >> b) & 1u) ? dpacc[r] * drop.scale : 0.0f;
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool ok = kbase + (unsigned)(32 * kb + 8 * (r >> 2) + (r & 3)) < kwidth;
+          const bool ok = allowed.ok(kb, r);
           const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));  // computed, then selected
           const float pv = ok ? e : 0.0f;
           sacc[r] = pv * (dpacc[r] - dvl);
@@ -500,6 +503,88 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
                   acc[db][4 * a + 2] * p.scale, acc[db][4 * a + 3] * p.scale);
       }
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// Mask probes of the backward (see launch_mask_probe_fwd for the forward's): the kernels'
+// decisions replayed with the functions they call, for one key token per wave (dK/dV
+// kernel) or one query token per wave (dQ kernel). A pair enters the gradient sums iff its
+// block is visited and not class 0, the lane test passes, and the query row exists (rows
+// past the sequence end carry LSE = +inf, so their weights are 0).
+// ---------------------------------------------------------------------------------------
+__global__ void mask_probe_bwd_kv_kernel(const int32_t* cu_q, const int32_t* cu_k, int num_seqs,
+                                         int mode, int window, int q0, int nq, int k0, int nk,
+                                         uint8_t* bits) {
+  const int u = k0 + blockIdx.x, lane = threadIdx.x, hg = lane >> 5;
+  const int s = seq_of_token(cu_k, num_seqs, u);
+  const SeqGeom g = load_geom(cu_q, cu_k, s, mode);
+  const int kj = u - g.k_start;
+  const int kt0 = (kj / BWD_BN) * BWD_BN, kt1 = min(kt0 + BWD_BN, g.len_k);
+  const int kw0 = kt0 + ((kj - kt0) / 32) * 32;
+  int kq_lo, kq_hi;
+  query_interval(kj, g, mode, window, kq_lo, kq_hi);
+  const unsigned kq_width = kq_hi > kq_lo ? (unsigned)(kq_hi - kq_lo) : 0u;
+  int qlo, qhi;
+  visible_queries(kt0, kt1, g, mode, window, qlo, qhi);
+  const int qstart = (qlo / BWD_BM) * BWD_BM;
+  const int nqt = qhi > qlo ? (qhi - qstart + BWD_BM - 1) / BWD_BM : 0;
+  for (int it = 0; it < nqt; ++it) {
+    const int qt0 = qstart + it * BWD_BM, qend = min(qt0 + BWD_BM, g.len_q);
+    for (int qh = 0; qh < 2; ++qh) {
+      const int qa = qt0 + 32 * qh, qz = min(qa + 32, qend);
+      const int cls = block_class(qa, qz, kw0, kw0 + 32, g, mode, window);
+      if (cls == 0) continue;
+      const KeyLaneTest allowed(qa, cls, hg, kq_lo, kq_width);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qp = qa + key_of_reg(r, hg);
+        const int t = g.q_start + qp;
+        if (allowed.ok(r) && qp < g.len_q && t >= q0 && t < q0 + nq)
+          bits[(size_t)(t - q0) * nk + blockIdx.x] = 1;
+      }
+    }
+  }
+}
+
+__global__ void mask_probe_bwd_q_kernel(const int32_t* cu_q, const int32_t* cu_k, int num_seqs,
+                                        int mode, int window, int q0, int nq, int k0, int nk,
+                                        uint8_t* bits) {
+  const int t = q0 + blockIdx.x, lane = threadIdx.x, hg = lane >> 5;
+  const int s = seq_of_token(cu_q, num_seqs, t);
+  const SeqGeom g = load_geom(cu_q, cu_k, s, mode);
+  const int pq = t - g.q_start;
+  const int p0 = (pq / FWD_BM) * FWD_BM, p1 = min(p0 + FWD_BM, g.len_q);
+  const int wp0 = p0 + ((pq - p0) / 32) * 32, wp1 = min(wp0 + 32, p1);
+  int kstart, nst;
+  stage_range(p0, p1, g, mode, window, FWD_BN, kstart, nst);
+  int kv_lo, kv_hi;
+  key_interval(pq, g, mode, window, kv_lo, kv_hi);
+  const unsigned kv_width = kv_hi > kv_lo ? (unsigned)(kv_hi - kv_lo) : 0u;
+  uint8_t* row = bits + (size_t)blockIdx.x * nk;
+  for (int st = 0; st < nst; ++st) {
+    const int kp = kstart + st * FWD_BN;
+    const int cls = block_class(wp0, wp1, kp, kp + FWD_BN, g, mode, window);
+    if (cls == 0) continue;
+    const QueryLaneTest allowed(kp, cls, hg, kv_lo, kv_width);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int u = g.k_start + kp + 32 * kb + key_of_reg(r, hg);
+        if (allowed.ok(kb, r) && u >= k0 && u < k0 + nk) row[u - k0] = 1;
+      }
+  }
+}
+
+hipError_t launch_mask_probe_bwd(const ProbeArgs& a, uint8_t* bits, hipStream_t st) {
+  hipError_t e = launch_probe_zero(bits, (long)a.nq * a.nk, st);
+  if (e != hipSuccess || a.nq == 0 || a.nk == 0) return e;
+  if (a.unit == 3)
+    hipLaunchKernelGGL(mask_probe_bwd_kv_kernel, dim3(a.nk), dim3(64), 0, st, a.cu_q, a.cu_k,
+                       a.num_seqs, a.mode, a.window, a.q0, a.nq, a.k0, a.nk, bits);
+  else
+    hipLaunchKernelGGL(mask_probe_bwd_q_kernel, dim3(a.nq), dim3(64), 0, st, a.cu_q, a.cu_k,
+                       a.num_seqs, a.mode, a.window, a.q0, a.nq, a.k0, a.nk, bits);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------

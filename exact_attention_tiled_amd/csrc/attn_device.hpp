@@ -151,6 +151,16 @@ __device__ __forceinline__ void visible_keys(int p0, int p1, const SeqGeom& g, i
   if (hi < lo) hi = lo;
 }
 
+// Stages of BN keys that query rows [p0, p1) visit: stage i covers key positions
+// [kstart + i BN, kstart + (i + 1) BN); nst = 0 when no key is visible.
+__device__ __forceinline__ void stage_range(int p0, int p1, const SeqGeom& g, int mode,
+                                            int window, int bn, int& kstart, int& nst) {
+  int klo, khi;
+  visible_keys(p0, p1, g, mode, window, klo, khi);
+  kstart = (klo / bn) * bn;
+  nst = khi > klo ? (khi - kstart + bn - 1) / bn : 0;
+}
+
 // Classification of a (query positions [p0,p1)) x (key positions [k0,k1)) block:
 // 0 = no pair allowed, 1 = some pairs (per-lane test needed), 2 = every pair allowed.
 __device__ __forceinline__ int block_class(int p0, int p1, int k0, int k1, const SeqGeom& g,
@@ -166,6 +176,63 @@ __device__ __forceinline__ int block_class(int p0, int p1, int k0, int k1, const
   if (window > 0 && k0 <= p1 - 1 + g.off - window) return 1;
   return 2;
 }
+
+// Split-K classification of one wave's KBW 32-key blocks at key position kw0 of a stage,
+// rows [rlo, rhi) of the group's G * len_q (position, head) rows, chunk keys [klo, khi):
+// returns the block class (0: the wave skips the stage) and sets clip when some keys of the
+// blocks lie outside the chunk (they belong to a neighbouring chunk's partial).
+template <int KBW>
+__device__ __forceinline__ int splitk_stage_class(int kw0, int klo, int khi, int rlo, int rhi,
+                                                  const SeqGeom& g, int G, int mode, int window,
+                                                  bool& clip) {
+  const int cw0 = max(kw0, klo), cw1 = min(kw0 + 32 * KBW, khi);
+  clip = cw0 != kw0 || cw1 != kw0 + 32 * KBW;
+  return (rhi <= rlo || cw1 <= cw0)
+             ? 0
+             : block_class(rlo / G, (rhi - 1) / G + 1, kw0, kw0 + 32 * KBW, g, mode, window);
+}
+
+// Split-K exclusion of keys outside the chunk for a classified stage (cls != 0); returns
+// whether the stage then needs the per-lane test (mask_blocks) of disallowed pairs.
+template <int KBW>
+__device__ __forceinline__ bool splitk_stage_clip(f32x16 (&s)[KBW], int cls, bool clip, int kw0,
+                                                  int klo, int khi, int lane) {
+  if (clip) {
+    const int cw0 = max(kw0, klo), cw1 = min(kw0 + 32 * KBW, khi);
+    const int hg = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < KBW; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kw0 + 32 * i + 8 * (r >> 2) + 4 * hg + (r & 3);
+        s[i][r] = ((kk >= cw0) & (kk < cw1)) ? s[i][r] : neg_inf();
+      }
+  }
+  return cls == 1 || clip;
+}
+
+// Backward element tests (the same logical mask as the forward). dK/dV kernel: this lane's
+// key has query interval [q_lo, q_lo + q_width) (query_interval); register r of a 32-query
+// block starting at qa holds query qa + 8 (r / 4) + 4 (lane / 32) + r % 4.
+struct KeyLaneTest {
+  unsigned base, width;
+  __device__ __forceinline__ KeyLaneTest(int qa, int cls, int hg, int q_lo, unsigned q_width)
+      : base((unsigned)(qa + 4 * hg - q_lo)), width(cls == 2 ? 0xffffffffu : q_width) {}
+  __device__ __forceinline__ bool ok(int r) const {
+    return base + (unsigned)(8 * (r >> 2) + (r & 3)) < width;
+  }
+};
+// dQ kernel: this lane's query has key interval [k_lo, k_lo + k_width) (key_interval);
+// register r of 32-key block kb of a stage at k0 holds key k0 + 32 kb + 8 (r / 4) +
+// 4 (lane / 32) + r % 4.
+struct QueryLaneTest {
+  unsigned base, width;
+  __device__ __forceinline__ QueryLaneTest(int k0, int cls, int hg, int k_lo, unsigned k_width)
+      : base((unsigned)(k0 + 4 * hg - k_lo)), width(cls == 2 ? 0xffffffffu : k_width) {}
+  __device__ __forceinline__ bool ok(int kb, int r) const {
+    return base + (unsigned)(32 * kb + 8 * (r >> 2) + (r & 3)) < width;
+  }
+};
 
 // Sequence owning packed token t: largest s with cu[s] <= t, skipping empty sequences.
 __device__ __forceinline__ int seq_of_token(const int32_t* cu, int num_seqs, int t) {
@@ -363,6 +430,36 @@ __device__ __forceinline__ int swz_key(int row) {
 template <int ROWB>
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ swz_key<ROWB>(row); }
 
+// Race exposure (test builds compiled with -DATTN_DEBUG_POISON_LDS). Every thread that is
+// about to refill an LDS buffer first overwrites exactly the bytes it will refill with a
+// finite sentinel (0x46EA46EA: about 3e4 read as fp32 and as each bf16 half), then refills
+// them (program order keeps the sentinel from landing after the data). The refill only
+// starts once the barrier that freed the buffer has passed, and readers of the new data
+// only read after the barrier that publishes it; were either barrier missing, a wave would
+// read the sentinel deterministically instead of the previous stage's plausible values.
+// Release builds compile the poisoning to nothing.
+constexpr int LDS_POISON = 0x46EA46EA;
+__device__ __forceinline__ void poison16(char* lds) {
+#if defined(ATTN_DEBUG_POISON_LDS)
+  *reinterpret_cast<i32x4*>(lds) = i32x4{LDS_POISON, LDS_POISON, LDS_POISON, LDS_POISON};
+#endif
+}
+__device__ __forceinline__ void poison8(char* lds) {
+#if defined(ATTN_DEBUG_POISON_LDS)
+  *reinterpret_cast<i32x2*>(lds) = i32x2{LDS_POISON, LDS_POISON};
+#endif
+}
+__device__ __forceinline__ void poison4(float* lds) {
+#if defined(ATTN_DEBUG_POISON_LDS)
+  *lds = __int_as_float(LDS_POISON);
+#endif
+}
+__device__ __forceinline__ void poison_done() {
+#if defined(ATTN_DEBUG_POISON_LDS)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
+}
+
 // Cache-policy operand of the DMA loads. CPOL_NT sets the nontemporal (streaming) hint for
 // data that one call reads exactly once: the split-K decode's K/V stream, which runs
 // 4-11 % faster with it on gfx950 (measured). Tiles that other workgroups re-read (prefill
@@ -394,6 +491,14 @@ struct DmaStager {
     // The buffer descriptor type exists only for the GPU target; the host pass never runs
     // this body and must not see it (it would drop kernel launch stubs).
 #if defined(__HIP_DEVICE_COMPILE__)
+#if defined(ATTN_DEBUG_POISON_LDS)
+    {
+      const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) poison16(lds_tile + (first_row + i * RPI) * ROWB + 16 * lane);
+      poison_done();
+    }
+#endif
     const int v = valid_rows < 0 ? 0 : (valid_rows > ROWS ? ROWS : valid_rows);
     // The descriptor must live in scalar registers: every operand is workgroup-uniform.
     const uint64_t base = (uint64_t)rows;
@@ -464,6 +569,15 @@ struct VtStager {
         r[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                              rsrc, (int)(voff + (uint32_t)u * row_stride), 0, 0));
     }
+#endif
+  }
+  // Race exposure: the sentinel into exactly the slots write() fills (see poison16).
+  __device__ __forceinline__ void poison(char* lds_tile) const {
+#if defined(ATTN_DEBUG_POISON_LDS)
+    if (!active) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) poison8(lds_tile + woff + e * PITCH);
+    poison_done();
 #endif
   }
   // Transpose the four loaded keys into eight V^T rows of 4 keys (8 bytes) each.

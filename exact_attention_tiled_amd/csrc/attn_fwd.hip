@@ -52,6 +52,7 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 // One online-softmax step for NK key blocks of 32 keys held in accumulator layout.
 // s[kb][r] is the raw (sign-folded) dot product of this lane's query with key
 // kpos0 + 32 kb + key_of_reg(r, g); pk receives P (not yet normalised) as the PV operand.
+// With need_mask the disallowed pairs are excluded first (mask_blocks).
 // m_run is in log2 units of the scaled logits; l_run is this lane's partial denominator
 // (the other half of the row lives in lane l ^ 32).
 // With DROP the denominator still sums every weight, and the PV operand carries
@@ -246,7 +247,8 @@ struct PrefillVStage<__bf16, D> {
   __device__ __forceinline__ void init(int, int, int tid, uint32_t rstride) {
     vt.init(tid, rstride);
   }
-  __device__ __forceinline__ void issue(const char* rows, int valid, uint32_t rstride, char*) {
+  __device__ __forceinline__ void issue(const char* rows, int valid, uint32_t rstride, char* tile) {
+    vt.poison(tile);  // (race-exposure builds only)
     vt.issue(rows, valid, rstride);
   }
   __device__ __forceinline__ void commit(char* tile) const { vt.write(tile); }
@@ -485,11 +487,14 @@ __device__ __forceinline__ void prefill_steady(const PipeCtx<D>& c, PipeRun<D>& 
   typedef Mma<__bf16, D> M;
   constexpr int BN = FWD_BN;
   const int kcur = c.kstart + j * BN;
-  // K_{j+1} (DMA) and V_j (registers). In the last iteration the K request covers no valid
-  // row: the descriptor's range check turns it into zero writes to a buffer nothing reads.
+  // K_{j+1} (DMA) and V_j (registers). In the last iteration the K request covers no row
+  // (a select, not a branch: a branch would split the block and stop the scheduler from
+  // spreading the requests over the MFMAs): the descriptor's range check turns it into zero
+  // writes to a buffer nothing reads, without fetching keys that no row of the tile sees.
   auto issue = [&]() {
-    c.dma.issue(c.kg + (size_t)(kcur + BN) * c.rstride, c.g.len_k - kcur - BN, c.rstride,
-                kbuf[B ^ 1]);
+    c.dma.issue(c.kg + (size_t)(kcur + BN) * c.rstride, j + 1 < c.nst ? c.g.len_k - kcur - BN : 0,
+                c.rstride, kbuf[B ^ 1]);
+    c.vst.poison(vbuf[B]);  // (race-exposure builds only) V^T_j lands there at the end
     c.vst.issue(c.vg + (size_t)kcur * c.rstride, c.g.len_k - kcur, c.rstride);
   };
   const float base = stage_max<D>(so, r.mask_prev, c.pq, kcur - BN, c.g, c.p.mode, c.p.window,
@@ -547,10 +552,8 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
   M::load_q(qr, qrow, qvalid, p.neg != 0, lane);
   const typename M::Offsets of = M::offsets(lane);
 
-  int klo, khi;
-  visible_keys(p0, p1, g, p.mode, p.window, klo, khi);
-  const int kstart = (klo / BN) * BN;
-  const int nst = khi > klo ? (khi - kstart + BN - 1) / BN : 0;
+  int kstart, nst;
+  stage_range(p0, p1, g, p.mode, p.window, BN, kstart, nst);
 
   const uint32_t rstride = (uint32_t)(p.hkv * D * 2);
   const char* kg = static_cast<const char*>(p.k) + ((size_t)g.k_start * p.hkv + kvh) * D * 2;
@@ -573,6 +576,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
     // K_0, V_0 and K_1 are all requested before the first wait: the tile's start costs one
     // memory round trip, not three.
     dma.issue(kg + (size_t)kstart * rstride, g.len_k - kstart, rstride, kbuf0);
+    vst.poison(vbuf0);
     vst.issue(vg + (size_t)kstart * rstride, g.len_k - kstart, rstride);
     if (nst > 1) {
       dma.issue(kg + (size_t)(kstart + BN) * rstride, g.len_k - kstart - BN, rstride, kbuf1);
@@ -670,33 +674,19 @@ struct SplitkWave {
                                         const typename M::QOperand (&qr)[M::QREGS],
                                         const typename M::Offsets& of, int lane) {
     constexpr int ROWB = M::ROWB;
-    const int G = p.group;
-    const int cw0 = max(kw0, klo), cw1 = min(kw0 + 32 * KBW, khi);
-    const int cls = (rhi <= rlo || cw1 <= cw0)
-                        ? 0
-                        : block_class(rlo / G, (rhi - 1) / G + 1, kw0, kw0 + 32 * KBW, g, p.mode,
-                                      p.window);
+    bool clip;
+    const int cls = splitk_stage_class<KBW>(kw0, klo, khi, rlo, rhi, g, p.group, p.mode,
+                                            p.window, clip);
     if (cls == 0) return;
-    // A key outside the chunk belongs to a neighbouring chunk's partial.
-    const bool clip = cw0 != kw0 || cw1 != kw0 + 32 * KBW;
     f32x16 sacc[KBW];
 #pragma unroll
     for (int i = 0; i < KBW; ++i) {
       sacc[i] = f32x16{};
       M::qk(sacc[i], kt + 32 * i * ROWB, qr, of, lane);
     }
-    if (clip) {
-      const int hg = lane >> 5;
-#pragma unroll
-      for (int i = 0; i < KBW; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = kw0 + 32 * i + key_of_reg(r, hg);
-          sacc[i][r] = ((kk >= cw0) & (kk < cw1)) ? sacc[i][r] : neg_inf();
-        }
-    }
+    const bool need_mask = splitk_stage_clip<KBW>(sacc, cls, clip, kw0, klo, khi, lane);
     typename M::PPack pk[KBW];
-    softmax_step<M, KBW, D>(sacc, pk, cls == 1 || clip, pq, kw0, g, p.mode, p.window, p.c2, m_run,
+    softmax_step<M, KBW, D>(sacc, pk, need_mask, pq, kw0, g, p.mode, p.window, p.c2, m_run,
                             l_run, o, lane);
 #pragma unroll
     for (int i = 0; i < KBW; ++i) M::pv(o, pk[i], vt + 32 * i * ROWB, of, lane);
@@ -912,31 +902,98 @@ __global__ __launch_bounds__(256) void splitk_combine_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------------------
-// Mask probe: the prefill kernel's decisions (stage range, per-wave block class, per-lane
-// test) replayed for single (query token, key token) pairs.
+// Mask probes. Each replays one kernel's exclusion decisions for a query token on a zero
+// score tile, with the functions that kernel calls in the same composition: its stage
+// range, the per-wave block class of every stage, and the per-lane tests (mask_blocks; the
+// split-K chunk clip). One 64-lane wave per query token t; its lanes hold t's query with
+// the two lane halves' key registers, as in the kernels. Every key whose score is still
+// finite (or whose block is wholly allowed) enters the softmax: bits[(t - q0) * nk +
+// (u - k0)] = 1 for it (the array is zeroed first).
 // ---------------------------------------------------------------------------------------
-__global__ void mask_probe_kernel(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int mode,
-                                  int window, int q0, int nq, int k0, int nk, uint8_t* bits) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)nq * nk) return;
-  const int t = q0 + (int)(idx / nk), u = k0 + (int)(idx % nk);
+__global__ void probe_zero_kernel(uint8_t* bits, long n) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    bits[i] = 0;
+}
+
+// Marks the keys of NK 32-key blocks at kpos0 (accumulator layout) whose score is finite.
+template <int NK>
+__device__ __forceinline__ void probe_mark(const f32x16 (&s)[NK], int kpos0, const SeqGeom& g,
+                                           int k0, int nk, uint8_t* row, int lane) {
+  const int hg = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int u = g.k_start + kpos0 + 32 * kb + key_of_reg(r, hg);
+      if (s[kb][r] != neg_inf() && u >= k0 && u < k0 + nk) row[u - k0] = 1;
+    }
+}
+
+// Prefill. PIPELINED: the bf16 kernel (every visited stage runs mask_blocks unless the
+// block class says every pair is allowed); otherwise the generic kernel (fp32, dropout:
+// class 0 stages are skipped, class 1 stages masked).
+template <bool PIPELINED>
+__global__ void mask_probe_prefill_kernel(const int32_t* cu_q, const int32_t* cu_k, int num_seqs,
+                                          int mode, int window, int q0, int nq, int k0, int nk,
+                                          uint8_t* bits) {
+  const int t = q0 + blockIdx.x, lane = threadIdx.x;
   const int s = seq_of_token(cu_q, num_seqs, t);
-  const SeqGeom g = load_geom_lane(cu_q, cu_k, s, mode);
+  const SeqGeom g = load_geom(cu_q, cu_k, s, mode);
   const int pq = t - g.q_start;
   const int p0 = (pq / FWD_BM) * FWD_BM, p1 = min(p0 + FWD_BM, g.len_q);
   const int wp0 = p0 + ((pq - p0) / 32) * 32, wp1 = min(wp0 + 32, p1);
-  int klo, khi;
-  visible_keys(p0, p1, g, mode, window, klo, khi);
-  const int kstart = (klo / FWD_BN) * FWD_BN;
-  const int nst = khi > klo ? (khi - kstart + FWD_BN - 1) / FWD_BN : 0;
-  uint8_t bit = 0;
-  const int pk = u - g.k_start;
-  if (u >= g.k_start && pk < g.len_k && pk >= kstart && pk < kstart + nst * FWD_BN) {
-    const int kt = kstart + ((pk - kstart) / FWD_BN) * FWD_BN;
-    const int cls = block_class(wp0, wp1, kt, kt + FWD_BN, g, mode, window);
-    bit = cls == 2 ? 1 : (cls == 1 ? (pair_allowed(pq, pk, g, mode, window) ? 1 : 0) : 0);
+  int kstart, nst;
+  stage_range(p0, p1, g, mode, window, FWD_BN, kstart, nst);
+  uint8_t* row = bits + (size_t)blockIdx.x * nk;
+  for (int st = 0; st < nst; ++st) {
+    const int kp = kstart + st * FWD_BN;
+    const int cls = block_class(wp0, wp1, kp, kp + FWD_BN, g, mode, window);
+    if (!PIPELINED && cls == 0) continue;
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    if (PIPELINED ? cls != 2 : cls == 1) mask_blocks<2>(sc, pq, kp, g, mode, window, lane);
+    probe_mark<2>(sc, kp, g, k0, nk, row, lane);
   }
-  bits[idx] = bit;
+}
+
+// Split-K decode with nsb key chunks of `chunk` keys per (sequence, K/V head), for query
+// head h: the rows of the group are (position, head-in-group) pairs, row pq * G + h % G;
+// its row block is owned by the waves w with w % NRB equal to it, each of which takes KBW
+// = NRB consecutive 32-key blocks of every 128-key stage.
+template <int NRB>
+__global__ void mask_probe_splitk_kernel(const int32_t* cu_q, const int32_t* cu_k, int num_seqs,
+                                         int mode, int window, int group, int h, int nsb,
+                                         int chunk, int q0, int nq, int k0, int nk,
+                                         uint8_t* bits) {
+  constexpr int KW = 4 / NRB, KBW = NRB, BN = SPLITK_STAGE;
+  const int t = q0 + blockIdx.x, lane = threadIdx.x;
+  const int s = seq_of_token(cu_q, num_seqs, t);
+  const SeqGeom g = load_geom(cu_q, cu_k, s, mode);
+  const int pq = t - g.q_start;
+  const int R = group * g.len_q;
+  const int r = pq * group + h % group;
+  const int rlo = (r / 32) * 32, rhi = min(R, rlo + 32);
+  int vlo, vhi;
+  visible_keys(0, g.len_q, g, mode, window, vlo, vhi);
+  uint8_t* row = bits + (size_t)blockIdx.x * nk;
+  for (int sigma = 0; sigma < nsb; ++sigma) {
+    const int klo = max(vlo, sigma * chunk), khi = min(vhi, sigma * chunk + chunk);
+    const int kstart = (klo / BN) * BN;
+    const int nst = khi > klo ? (khi - kstart + BN - 1) / BN : 0;
+    for (int st = 0; st < nst; ++st)
+      for (int kwi = 0; kwi < KW; ++kwi) {
+        const int kw0 = kstart + st * BN + 32 * kwi * KBW;
+        bool clip;
+        const int cls = splitk_stage_class<KBW>(kw0, klo, khi, rlo, rhi, g, group, mode, window,
+                                                clip);
+        if (cls == 0) continue;
+        f32x16 sc[KBW];
+#pragma unroll
+        for (int i = 0; i < KBW; ++i) sc[i] = f32x16{};
+        if (splitk_stage_clip<KBW>(sc, cls, clip, kw0, klo, khi, lane))
+          mask_blocks<KBW>(sc, pq, kw0, g, mode, window, lane);
+        probe_mark<KBW>(sc, kw0, g, k0, nk, row, lane);
+      }
+  }
 }
 
 // keep[i * nk + j] = 1 iff element (query position q0 + i, key position k0 + j) of sequence
@@ -979,10 +1036,8 @@ __device__ __forceinline__ int slot_cost(const int32_t* cu_q, const int32_t* cu_
   if (j >= ntiles) return -1;
   const int tile = ntiles - 1 - j;
   const int p0 = tile * BM, p1 = min(p0 + BM, g.len_q);
-  int klo, khi;
-  visible_keys(p0, p1, g, mode, window, klo, khi);
-  const int kstart = (klo / FWD_BN) * FWD_BN;
-  const int nst = khi > klo ? (khi - kstart + FWD_BN - 1) / FWD_BN : 0;
+  int kstart, nst;
+  stage_range(p0, p1, g, mode, window, FWD_BN, kstart, nst);
   return min(nst, ORDER_BUCKETS - 1);
 }
 
@@ -1158,13 +1213,31 @@ hipError_t launch_fwd_splitk(const FwdArgs& a, int nsb, int chunk, void* ws, hip
   return a.d == 64 ? splitk_typed<float, 64>(a, nsb, chunk, ws, st) : hipErrorNotSupported;
 }
 
-hipError_t launch_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int mode,
-                             int window, int q0, int nq, int k0, int nk, uint8_t* bits,
-                             hipStream_t st) {
-  const long n = (long)nq * nk;
-  const int grid = (int)((n + 255) / 256);
-  hipLaunchKernelGGL(mask_probe_kernel, dim3(grid), dim3(256), 0, st, cu_q, cu_k, num_seqs, mode,
-                     window, q0, nq, k0, nk, bits);
+hipError_t launch_probe_zero(uint8_t* bits, long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long blocks = std::min<long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(probe_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, bits, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_probe_fwd(const ProbeArgs& a, uint8_t* bits, hipStream_t st) {
+  hipError_t e = launch_probe_zero(bits, (long)a.nq * a.nk, st);
+  if (e != hipSuccess || a.nq == 0) return e;
+  const dim3 grid(a.nq), block(64);
+  if (a.unit == 0)
+    hipLaunchKernelGGL((mask_probe_prefill_kernel<true>), grid, block, 0, st, a.cu_q, a.cu_k,
+                       a.num_seqs, a.mode, a.window, a.q0, a.nq, a.k0, a.nk, bits);
+  else if (a.unit == 1)
+    hipLaunchKernelGGL((mask_probe_prefill_kernel<false>), grid, block, 0, st, a.cu_q, a.cu_k,
+                       a.num_seqs, a.mode, a.window, a.q0, a.nq, a.k0, a.nk, bits);
+  else if (a.nrb == 1)
+    hipLaunchKernelGGL((mask_probe_splitk_kernel<1>), grid, block, 0, st, a.cu_q, a.cu_k,
+                       a.num_seqs, a.mode, a.window, a.group, a.head, a.nsb, a.chunk, a.q0, a.nq,
+                       a.k0, a.nk, bits);
+  else
+    hipLaunchKernelGGL((mask_probe_splitk_kernel<2>), grid, block, 0, st, a.cu_q, a.cu_k,
+                       a.num_seqs, a.mode, a.window, a.group, a.head, a.nsb, a.chunk, a.q0, a.nq,
+                       a.k0, a.nk, bits);
   return hipGetLastError();
 }
 

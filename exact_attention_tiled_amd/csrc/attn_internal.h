@@ -62,9 +62,20 @@ size_t splitk_workspace_bytes(int nsplit_eff, int total_q, int hq, int d);
 hipError_t launch_fwd_splitk(const FwdArgs& a, int blocks_per_kvh, int chunk, void* workspace,
                              hipStream_t stream);
 
-hipError_t launch_mask_probe(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int mode,
-                             int window, int q0, int nq, int k0, int nk, uint8_t* bits,
-                             hipStream_t stream);
+// Mask probes (one kernel unit's exclusion decisions replayed into a uint8 [nq, nk] array;
+// include/attn.h, attn_mask_probe_ex). unit: 0 bf16 prefill, 1 generic prefill (fp32,
+// dropout), 2 split-K decode (plan nsb / chunk / nrb, query head `head`), 3 backward dK/dV
+// kernel, 4 backward dQ kernel.
+struct ProbeArgs {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int num_seqs, mode, window, unit;
+  int group, head, nsb, chunk, nrb;  // split-K only
+  int q0, nq, k0, nk;
+};
+hipError_t launch_probe_zero(uint8_t* bits, long n, hipStream_t stream);
+hipError_t launch_mask_probe_fwd(const ProbeArgs& a, uint8_t* bits, hipStream_t stream);
+hipError_t launch_mask_probe_bwd(const ProbeArgs& a, uint8_t* bits, hipStream_t stream);
 
 // Backward tile shape and workspace.
 size_t bwd_workspace_bytes(int total_q, int hq, int d);

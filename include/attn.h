@@ -246,18 +246,49 @@ int attn_dropout_probe(int32_t seq, int32_t head, int32_t q0, int32_t nq, int32_
                        void* stream);
 
 /*
- * attn_mask_probe - runs the forward kernels' mask unit (tile range selection plus the
- * per-lane test, with the prefill tile shape) for query tokens [q0, q0 + nq) against key
- * tokens [k0, k0 + nk) and writes bits[i * nk + j] = 1 if the pair (q0 + i, k0 + j) enters
- * the softmax, else 0 (uint8, device memory, nq * nk bytes). Exists so the mask can be
- * compared bit for bit with an explicit mask built from sequence ids and positions.
- * Returns ATTN_ERR_BAD_RANGE if the window leaves [0, total_q) x [0, total_k).
+ * attn_mask_probe - replays the bf16 forward prefill's mask decisions (its stage range, the
+ * per-wave block class of every stage and the per-lane test of the kernel) for query tokens
+ * [q0, q0 + nq) against key tokens [k0, k0 + nk) and writes bits[i * nk + j] = 1 if the pair
+ * (q0 + i, k0 + j) enters the softmax, else 0 (uint8, device memory, nq * nk bytes). Exists so
+ * the mask can be compared bit for bit with an explicit mask built from sequence ids and
+ * positions (Causal Mask and Ragged Sequence Layouts, sections 1-4). Same as
+ * attn_mask_probe_ex with ATTN_PROBE_PREFILL. Returns ATTN_ERR_BAD_RANGE if the window leaves
+ * [0, total_q) x [0, total_k).
  */
 int attn_mask_probe(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                     int32_t num_seqs, int32_t total_q, int32_t total_k,
                     int32_t mask_mode, int32_t window,
                     int32_t q0, int32_t nq, int32_t k0, int32_t nk,
                     uint8_t* bits, void* stream);
+
+/* Kernel units whose mask decisions attn_mask_probe_ex replays. */
+enum attn_probe_unit {
+  ATTN_PROBE_PREFILL = 0,          /* bf16 prefill (software-pipelined kernel) */
+  ATTN_PROBE_PREFILL_GENERIC = 1,  /* fp32 prefill and every dropout forward */
+  ATTN_PROBE_SPLITK = 2,           /* split-K decode: chunk clip + per-lane test, one head */
+  ATTN_PROBE_BWD_KV = 3,           /* backward dK / dV kernel (keys on lanes) */
+  ATTN_PROBE_BWD_Q = 4             /* backward dQ kernel (queries on lanes) */
+};
+
+/*
+ * attn_mask_probe_ex - attn_mask_probe for any kernel unit: the unit's own composition of
+ * stage ranges, block classes and per-lane tests (the backward's, which rebuild the
+ * forward's logical mask: Causal Mask and Ragged Sequence Layouts, section 6), replayed into
+ * bits as above. For the backward units a pair counts if it enters the gradient sums (rows
+ * past a sequence's end never do). ATTN_PROBE_SPLITK replays the split-K plan attn_fwd_ex
+ * chooses for these shapes with num_splits key chunks (0 = the automatic count; bf16,
+ * head_dim 128) for query head `head` (the row blocks of a GQA group depend on it); it
+ * needs max_seqlen_q/k, Hq and Hkv as for attn_fwd and returns ATTN_ERR_BAD_PLAN where the
+ * split-K path does not apply. The other units ignore max_seqlen_q/k, Hq, Hkv, head and
+ * num_splits. Errors: ATTN_ERR_BAD_PLAN for an unknown unit, otherwise as attn_mask_probe.
+ */
+int attn_mask_probe_ex(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int32_t num_seqs, int32_t total_q, int32_t total_k,
+                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t num_heads_q, int32_t num_heads_kv,
+                       int32_t mask_mode, int32_t window, int32_t unit, int32_t head,
+                       int32_t num_splits, int32_t q0, int32_t nq, int32_t k0, int32_t nk,
+                       uint8_t* bits, void* stream);
 
 /*
  * attn_describe_plan - writes a one-line description of what attn_fwd_ex would launch for

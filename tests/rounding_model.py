@@ -1,0 +1,82 @@
+"""CPU model of the roundings the bf16 kernels prescribe, applied to exact (float64) values.
+
+Test infrastructure for deriving gradient tolerances: it is neither the oracle nor the HIP
+path. Every value is first computed exactly (float64), then rounded to bf16 (round to
+nearest even) at exactly the points where the kernels hold bf16 data:
+  forward  O = (sum_j bf16(p_j) v_j) / sum_j p_j, stored as bf16 (the PV contraction takes
+           the unnormalised weights as bf16 operands, the denominator sums them unrounded);
+  backward P rebuilt from the LSE, D = rowsum(dO * O_stored) (without dropout) or the exact
+           D = sum_j P dP (the dropout path's own D pass), dS = P (dP - D) and the dV operand
+           (P, or Z = P * keep / (1 - p) with dropout) rounded to bf16 before the
+           contractions; dQ, dK, dV accumulated exactly and stored as bf16.
+The fp32 accumulations of the kernels (products of bf16 values are exact in fp32; sums carry
+relative errors near 2^-24) are left exact here: they are orders of magnitude below the
+bf16 roundings.
+
+The tolerance a kernel output needs, as atol at rtol 2e-2 (|err| <= atol + 2e-2 |ref|), is
+then what this model needs on the same inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads as wl
+
+RTOL = 2e-2
+
+
+def bf16(x):
+    return wl.round_to_bf16(np.asarray(x, dtype=np.float32)).astype(np.float64)
+
+
+def required_atol(got, ref):
+    """Smallest atol with |got - ref| <= atol + RTOL |ref| everywhere (0 if none needed)."""
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    return float(max(0.0, (err - RTOL * np.abs(ref)).max())) if err.size else 0.0
+
+
+def model_backward(w, dropout_p=0.0, seed=0):
+    """(dQ, dK, dV) of the rounding model for workload w (bf16 inputs, any mask, GQA)."""
+    q, k, v, do = (np.asarray(a, np.float64) for a in (w.q, w.k, w.v, w.dout))
+    thr = oracle.dropout_threshold(dropout_p)
+    zscale = float(np.float32(256.0 / (256 - thr))) if thr > 0 else 1.0
+    hq, hkv = q.shape[1], k.shape[1]
+    grp = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    sq, pq, lq = oracle.token_metadata(w.cu_q)
+    sk, pk, lk = oracle.token_metadata(w.cu_k)
+    for s in range(len(lq)):
+        qa, qb, ka, kb = (int(x) for x in (w.cu_q[s], w.cu_q[s + 1], w.cu_k[s], w.cu_k[s + 1]))
+        if qa == qb or ka == kb:
+            continue
+        a = oracle.allowed(sq[qa:qb, None], pq[qa:qb, None], sk[None, ka:kb], pk[None, ka:kb],
+                           lq[s], lk[s], w.mask_mode, w.window)
+        rows = a.any(axis=1)
+        for h in range(hq):
+            g = h // grp
+            logits = np.where(a, w.scale * q[qa:qb, h] @ k[ka:kb, g].T, -np.inf)
+            m = np.where(rows, logits.max(axis=1, initial=-np.inf), 0.0)[:, None]
+            pt = np.where(a, np.exp(logits - m), 0.0)
+            l = pt.sum(axis=1, keepdims=True)
+            l1 = np.where(l > 0, l, 1.0)
+            p = pt / l1
+            if thr > 0:
+                keep = oracle.dropout_keep(seed, s, h, pq[qa:qb, None], pk[None, ka:kb], thr)
+                zf = np.where(keep, zscale, 0.0)
+            else:
+                zf = 1.0
+            dp = (do[qa:qb, h] @ v[ka:kb, g].T) * zf
+            if thr > 0:
+                dd = (p * dp).sum(axis=1)                       # the dropout path's exact D
+            else:
+                o = bf16((bf16(pt) @ v[ka:kb, g]) / l1)        # the stored forward output
+                dd = (do[qa:qb, h] * o).sum(axis=1)
+            ds = bf16(p * (dp - dd[:, None]))
+            z = bf16(p * zf)
+            dq[qa:qb, h] = w.scale * ds @ k[ka:kb, g]
+            dk[ka:kb, g] += w.scale * ds.T @ q[qa:qb, h]
+            dv[ka:kb, g] += z.T @ do[qa:qb, h]
+    return bf16(dq), bf16(dk), bf16(dv)

@@ -80,7 +80,10 @@ def test_fwd_workspace_checks(lib):
     assert need > 0
     assert _fwd(lib, num_seqs=2, total_q=2, total_k=4096, max_q=1, max_k=2048, hq=8, hkv=2,
                 d=128, mode=2, path=2, ws=1, wsb=need - 1) == WS_SMALL
+    # prefill of equal lengths needs none; unequal lengths one int32 per tile slot
+    # (256 // 128 + 2 slots), rounded up to 256 bytes
     assert lib.attn_fwd_ex_workspace_size(2, 256, 256, 128, 128, 2, 2, 64, 1, 2, 0, 1, 0) == 0
+    assert lib.attn_fwd_ex_workspace_size(2, 256, 300, 200, 200, 2, 2, 64, 0, 2, 0, 1, 0) == 256
 
 
 def test_bwd_validation(lib):
@@ -185,3 +188,18 @@ def test_no_workspace_validation(lib):
     assert need > (16 << 20)
     assert call(**big) == SCRATCH_SMALL
     assert call(a5=0) == OK           # empty batch: nothing to do
+
+
+def test_mask_probe_ex_validation(lib):
+    """Unknown units and split-K shapes the decode path does not take are refused on the
+    host; so are heads outside [0, Hq) and windows outside the token ranges."""
+    def call(unit, hq=8, hkv=2, max_q=4, max_k=300, head=0, q0=0, nq=4, k0=0, nk=300):
+        return lib.attn_mask_probe_ex(1, 1, 1, 4, 300, max_q, max_k, hq, hkv, 2, 0, unit, head,
+                                      0, q0, nq, k0, nk, 1, None)
+    assert call(5) == BAD_PLAN
+    assert call(-1) == BAD_PLAN
+    assert call(2, hq=32, hkv=1) == BAD_PLAN   # 128 rows per K/V head: prefill only
+    assert call(2, head=8) == BAD_RANGE
+    assert call(0, nq=5) == BAD_RANGE
+    assert call(3, k0=1) == BAD_RANGE
+    assert call(2, hq=6, hkv=4) == BAD_HEADS

@@ -108,24 +108,30 @@ def test_bwd_canaries_no_out_of_bounds_writes():
 @pytest.mark.parametrize("window", [0, 1024])
 def test_train_full_size(window):
     """B=2, Hq=32, Hkv=8, N=8192, d=128, causal top-left (and window 1024): full GPU
-    forward + backward; oracle on one (sequence, K/V head group) slice: O, LSE of its 4
-    query heads and dQ, dK, dV of the whole group."""
+    forward + backward; against the oracle on both sequences x two K/V head groups: O, LSE of
+    the groups' query heads and dQ, dK, dV of the whole groups (slices evaluated in parallel
+    CPU workers)."""
+    import oracle_pool as op
     w = wl.train_bf16(window=window)
     t = to_device(w)
     out, lse = run_fwd(w, t)
     dq, dk, dv = run_bwd(w, t, out, lse)
     o, l = to_np(out), to_np(lse)
     gq, gk, gv = to_np(dq), to_np(dk), to_np(dv)
+    del t, out, lse, dq, dk, dv
     for x in (o, l, gq, gk, gv):
         assert np.all(np.isfinite(x))
-    s, g = 1, 3
-    heads = list(range(4 * g, 4 * g + 4))
-    ref_o, ref_l = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode,
-                                    w.window, seqs=[s], heads=heads)
-    rq, rk, rv = _oracle_bwd(w, seqs=[s], kv_heads=[g])
-    rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
-    assert_close(o[rows][:, heads], ref_o[rows][:, heads], *BF16_TOL, "train O")
-    assert_close(l[heads][:, rows], ref_l[heads][:, rows], 1e-3, 0.0, "train LSE")
-    assert_close(gq[rows][:, heads], rq[rows][:, heads], *BF16_TOL, "train dQ")
-    assert_close(gk[rows][:, g], rk[rows][:, g], *BF16_TOL, "train dK")
-    assert_close(gv[rows][:, g], rv[rows][:, g], *BF16_TOL, "train dV")
+    slices = [(s, g) for s in (0, 1) for g in (0, 5)]
+    tasks = [(op.fwd_slice, (s, list(range(4 * g, 4 * g + 4)))) for s, g in slices]
+    tasks += [(op.bwd_slice, (s, g)) for s, g in slices]
+    print(f"train full size window={window}: {len(tasks)} oracle tasks", flush=True)
+    res = op.run("train_bf16", {"window": window}, tasks)
+    for (s, g), (ro, rl), (rq, rk, rv) in zip(slices, res[:4], res[4:]):
+        heads = list(range(4 * g, 4 * g + 4))
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+        krows = slice(int(w.cu_k[s]), int(w.cu_k[s + 1]))
+        assert_close(o[rows][:, heads], ro, *BF16_TOL, f"train O s{s} g{g}")
+        assert_close(l[heads][:, rows], rl, 1e-3, 0.0, f"train LSE s{s} g{g}")
+        assert_close(gq[rows][:, heads], rq, *BF16_TOL, f"train dQ s{s} g{g}")
+        assert_close(gk[krows][:, g], rk, *BF16_TOL, f"train dK s{s} g{g}")
+        assert_close(gv[krows][:, g], rv, *BF16_TOL, f"train dV s{s} g{g}")

@@ -5,7 +5,9 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_util import BF16_TOL, LSE_TOL, assert_close, to_device, to_np, tol_for
+from gpu_util import (BF16_TOL, DROPOUT_GRAD_TOL, LSE_TOL, assert_close, to_device, to_np,
+                      tol_for)
+from rounding_model import required_atol
 
 pytestmark = pytest.mark.gpu
 
@@ -52,11 +54,11 @@ EDGE = [0, 1, 63, 64, 65, 127, 128, 129]
 
 # The backward's contractions take Z = P * keep / (1 - p) (dV) and dS (dK, dQ) as bf16
 # operands. On the edge workloads below - one sequence sums about 400 rounded weights near
-# 0.4 into every dV entry of its 3 keys - those roundings alone, applied to the oracle's
-# fp64 values, move 12 gradient elements beyond 2e-2 + 2e-2 |ref| and stay within 0.59 of
-# 6e-2 + 2e-2 |ref| (tests/test_tolerance_derivation.py, CPU). The edge backward is held to
-# that bound; outputs, LSE, the realisation and the full-size gradients to the standard ones.
-DROPOUT_GRAD_TOL = (6e-2, 2e-2)
+# 0.4 into every dV entry of its 3 keys - those roundings alone move some gradients beyond
+# 2e-2 + 2e-2 |ref|. The edge backward is held to DROPOUT_GRAD_TOL (gpu_util), the bound the
+# CPU rounding model derives for exactly these workloads (test_tolerance_derivation.py);
+# outputs, LSE, the realisation, the canary workload and the full-size gradients keep the
+# standard bounds.
 
 
 
@@ -100,7 +102,8 @@ def test_dropout_backward_edges(d, mode, window):
                                w.window, dropout_p=p, seed=seed)
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         worst = assert_close(to_np(g), r, *DROPOUT_GRAD_TOL, f"dropout {name}")
-        print(f"dropout {name}: {worst}", flush=True)
+        print(f"dropout {name}: max |err| {worst:.4f}, required atol at rtol 2e-2 "
+              f"{required_atol(to_np(g), r):.4f} (bound {DROPOUT_GRAD_TOL[0]})", flush=True)
 
 
 def test_dropout_replays_across_packings():
@@ -213,4 +216,4 @@ def test_dropout_canaries_no_out_of_bounds_writes():
     ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
                                w.window, dropout_p=0.25, seed=777)
     for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
-        assert_close(to_np(g), r, *DROPOUT_GRAD_TOL, f"dropout canary {name}")
+        assert_close(to_np(g), r, *BF16_TOL, f"dropout canary {name}")

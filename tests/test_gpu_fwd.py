@@ -38,20 +38,64 @@ MASK_PACKS = [
 ]
 
 
+PROBE_UNITS = {0: "prefill_bf16", 1: "prefill_generic", 3: "bwd_dk_dv", 4: "bwd_dq"}
+
+
+@pytest.mark.parametrize("unit", sorted(PROBE_UNITS), ids=lambda u: PROBE_UNITS[u])
 @pytest.mark.parametrize("pack", range(len(MASK_PACKS)))
 @pytest.mark.parametrize("mode,window", [(0, 0), (1, 0), (2, 0), (1, 1), (1, 64), (2, 7), (2, 130)])
-def test_mask_probe_bit_exact(pack, mode, window):
+def test_mask_probe_bit_exact(pack, mode, window, unit):
+    """Each kernel unit's own mask decisions (stage range, block classes, per-lane tests)
+    against the explicit mask from sequence ids and positions, bit for bit ("Causal Mask
+    and Ragged Sequence Layouts", sections 1-4; section 6 for the backward units)."""
     import torch
     import exact_attention_tiled_amd as eat
     lq, lk = MASK_PACKS[pack]
     cu_q, cu_k = wl.cu_from_lengths(lq), wl.cu_from_lengths(lk)
     tq, tk = int(cu_q[-1]), int(cu_k[-1])
-    print(f"mask probe pack={pack} mode={mode} window={window}", flush=True)
-    bits = eat.attn_mask_probe(torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda(),
-                               tq, tk, mode, window, 0, tq, 0, tk)
+    print(f"mask probe unit={PROBE_UNITS[unit]} pack={pack} mode={mode} window={window}", flush=True)
+    cq, ck = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    if unit == eat.ATTN_PROBE_PREFILL:
+        bits = eat.attn_mask_probe(cq, ck, tq, tk, mode, window, 0, tq, 0, tk)
+    else:
+        bits = eat.attn_mask_probe_ex(cq, ck, tq, tk, max(lq), max(lk), 1, 1, mode, window, unit,
+                                      0, tq, 0, tk)
     got = bits.cpu().numpy().astype(bool)
     want = oracle.explicit_mask(cu_q, cu_k, mode, window)
     assert np.array_equal(got, want), np.argwhere(got != want)[:10].tolist()
+
+
+# Decode-shaped packs for the split-K unit: query lengths, key lengths, Hq, Hkv (G * max
+# query length <= 64 rows per K/V head, one or two 32-row blocks).
+SPLITK_PACKS = [
+    ([1, 4, 16, 0, 3], [300, 129, 1000, 5, 2], 8, 2),
+    ([64, 1, 7], [32, 300, 7], 2, 2),
+    ([16, 16], [4096, 3000], 8, 2),
+    ([5, 9], [700, 9], 6, 1),
+]
+
+
+@pytest.mark.parametrize("pack", range(len(SPLITK_PACKS)))
+@pytest.mark.parametrize("mode,window", [(2, 0), (1, 0), (0, 0), (2, 300), (2, 7)])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_mask_probe_splitk_bit_exact(pack, mode, window, splits):
+    """The split-K decode's decisions (chunk ranges, the chunk clip, block classes of the
+    row blocks, per-lane tests) for every query head of the group against the explicit
+    mask, for the automatic and forced split counts."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    lq, lk, hq, hkv = SPLITK_PACKS[pack]
+    cu_q, cu_k = wl.cu_from_lengths(lq), wl.cu_from_lengths(lk)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    cq, ck = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    want = oracle.explicit_mask(cu_q, cu_k, mode, window)
+    print(f"split-K mask probe pack={pack} mode={mode} window={window} splits={splits}", flush=True)
+    for h in range(hq // hkv):
+        bits = eat.attn_mask_probe_ex(cq, ck, tq, tk, max(lq), max(lk), hq, hkv, mode, window,
+                                      eat.ATTN_PROBE_SPLITK, 0, tq, 0, tk, head=h,
+                                      num_splits=splits)
+        got = bits.cpu().numpy().astype(bool)
+        assert np.array_equal(got, want), (h, np.argwhere(got != want)[:10].tolist())
 
 
 # ----------------------------------------------------------------------------------------
@@ -259,41 +303,54 @@ def test_unusual_scales(scale):
 # ----------------------------------------------------------------------------------------
 
 def test_dense_bf16_full_size():
-    """B=4, H=16, N=2048, d=128, causal top-left; oracle on 3 (sequence, head) slices."""
+    """B=4, H=16, N=2048, d=128, causal top-left: O and LSE of every (sequence, head) slice
+    against the oracle (slices evaluated in parallel CPU workers)."""
+    import oracle_pool as op
     w = wl.dense_bf16()
     out, lse = run_fwd(w)
     o, l = to_np(out), to_np(lse)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
-    for s, h in ((0, 0), (2, 7), (3, 15)):
-        ref_o, ref_l = _oracle(w, seqs=[s], heads=[h])
+    tasks = [(op.fwd_slice, (s, list(range(h0, h0 + 4)))) for s in range(4) for h0 in range(0, 16, 4)]
+    print(f"dense full size: {len(tasks)} oracle tasks", flush=True)
+    for (_, (s, heads)), (ro, rl) in zip(tasks, op.run("dense_bf16", {}, tasks)):
         rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
-        assert_close(o[rows, h], ref_o[rows, h], *BF16_TOL, f"dense O s{s} h{h}")
-        assert_close(l[h, rows], ref_l[h, rows], LSE_TOL, 0.0, f"dense LSE s{s} h{h}")
+        assert_close(o[rows][:, heads], ro, *BF16_TOL, f"dense O s{s} h{heads}")
+        assert_close(l[heads][:, rows], rl, LSE_TOL, 0.0, f"dense LSE s{s} h{heads}")
 
 
 def test_ragged_gqa_full_size():
-    """16384 packed tokens, ragged lengths incl. 63/64/65/127/128/129, Hq=32, Hkv=8; oracle
-    on every short sequence and on the longest, over heads spanning several GQA groups."""
+    """16384 packed tokens, ragged lengths incl. 63/64/65/127/128/129, Hq=32, Hkv=8, V offset
+    per sequence: every sequence on one query head of each of the 8 GQA groups, and all 32
+    heads of the three longest sequences, against the oracle ("Causal Mask and Ragged
+    Sequence Layouts", fifth section: packed against per-sequence with distinct value
+    ranges)."""
+    import oracle_pool as op
     w = wl.ragged_gqa()
     out, lse = run_fwd(w)
     o, l = to_np(out), to_np(lse)
     assert np.all(np.isfinite(o))
     lens = np.diff(w.cu_q)
-    seqs = [int(s) for s in np.nonzero(lens <= 129)[0]] + [int(np.argmax(lens))]
-    heads = [0, 3, 4, 13, 31]
-    ref_o, ref_l = _oracle(w, seqs=seqs, heads=heads)
-    for s in seqs:
+    longest = [int(x) for x in np.argsort(lens)[-3:]]
+    tasks = []
+    for s in range(w.num_seqs):
+        if s in longest:
+            tasks += [(op.fwd_slice, (s, list(range(h0, h0 + 8)))) for h0 in range(0, 32, 8)]
+        else:
+            tasks.append((op.fwd_slice, (s, [4 * g + g % 4 for g in range(8)])))
+    print(f"ragged full size: {w.num_seqs} sequences, {len(tasks)} oracle tasks", flush=True)
+    for (_, (s, heads)), (ro, rl) in zip(tasks, op.run("ragged_gqa", {}, tasks)):
         rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
-        for h in heads:
-            assert_close(o[rows, h], ref_o[rows, h], *BF16_TOL, f"ragged O s{s} h{h}")
-            assert_close(l[h, rows], ref_l[h, rows], LSE_TOL, 0.0, f"ragged LSE s{s} h{h}")
+        assert_close(o[rows][:, heads], ro, *BF16_TOL, f"ragged O s{s} h{heads}")
+        assert_close(l[heads][:, rows], rl, LSE_TOL, 0.0, f"ragged LSE s{s} h{heads}")
 
 
 @pytest.mark.parametrize("nq", [1, 4, 16])
 def test_decode_full_size(nq):
-    """B=16, Hq=32, Hkv=8, d=128, Nk=32768, bottom-right; oracle on 3 (sequence, K/V head)
-    groups; the auto plan must pick the split-K path."""
+    """B=16, Hq=32, Hkv=8, d=128, Nk=32768, bottom-right: every sequence, each on one K/V
+    head group (all of the group's query heads), against the oracle; the auto plan must
+    pick the split-K path."""
     import exact_attention_tiled_amd as eat
+    import oracle_pool as op
     w = wl.decode(nq)
     t = to_device(w)
     plan = eat.attn_describe_plan(t["q"], t["k"], t["cu_q"], w.max_seqlen_q, w.max_seqlen_k,
@@ -302,9 +359,9 @@ def test_decode_full_size(nq):
     out, lse = run_fwd(w, t)
     o, l = to_np(out), to_np(lse)
     del t
-    for s, g in ((0, 0), (7, 5), (15, 7)):
-        heads = list(range(4 * g, 4 * g + 4))
-        ref_o, ref_l = _oracle(w, seqs=[s], heads=heads)
+    tasks = [(op.fwd_slice, (s, list(range(4 * (s % 8), 4 * (s % 8) + 4)))) for s in range(16)]
+    # two workers: each regenerates the 2 GiB cache, and the slices themselves are small
+    for (_, (s, heads)), (ro, rl) in zip(tasks, op.run("decode", {"nq": nq}, tasks, procs=2)):
         rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
-        assert_close(o[rows][:, heads], ref_o[rows][:, heads], *BF16_TOL, f"decode O s{s} g{g}")
-        assert_close(l[heads][:, rows], ref_l[heads][:, rows], LSE_TOL, 0.0, f"decode LSE s{s}")
+        assert_close(o[rows][:, heads], ro, *BF16_TOL, f"decode O s{s} h{heads}")
+        assert_close(l[heads][:, rows], rl, LSE_TOL, 0.0, f"decode LSE s{s} h{heads}")

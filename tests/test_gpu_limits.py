@@ -5,7 +5,9 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_util import BF16_TOL, LSE_TOL, assert_close, run_fwd, to_device, to_np
+from gpu_util import (BF16_TOL, GQA64_GRAD_TOL, LSE_TOL, assert_close, run_fwd, to_device,
+                      to_np)
+from rounding_model import required_atol
 
 pytestmark = pytest.mark.gpu
 
@@ -97,14 +99,11 @@ def test_many_tiny_sequences(mode):
         assert_close(to_np(g), r, *BF16_TOL, f"tiny pack {name}")
 
 
-# dK and dV of this workload's first keys sum 64 heads x up to 300 queries of large terms
-# (sum |P dO| reaches 330). The roundings the backward's arithmetic prescribes - P and dS
-# as bf16 MFMA operands, D = rowsum(dO * O) formed from the bf16 output, P rebuilt from an
-# LSE that is itself within 1e-3 - move those entries by up to 0.04-0.05 when applied to
-# the fp64 oracle's own values on the CPU (test_tolerance_derivation.py), beyond
-# 2e-2 + 2e-2 |ref| for a few elements. dK and dV are therefore held to 8e-2 + 2e-2 |ref| here; O, LSE and dQ
-# to the standard bound.
-GQA64_GRAD_TOL = (8e-2, 2e-2)
+# dK and dV of this workload's first keys sum 64 heads x up to 300 queries of large terms.
+# The bf16 rounding of the P and dS operands and of the stored gradients alone moves some of
+# them beyond 2e-2 + 2e-2 |ref|; GQA64_GRAD_TOL (gpu_util) is the bound the CPU rounding model
+# derives for exactly this workload (test_tolerance_derivation.py). O, LSE and dQ keep the
+# standard bound.
 
 
 def test_gqa_group_of_64():
@@ -126,7 +125,8 @@ def test_gqa_group_of_64():
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         tol = GQA64_GRAD_TOL if name in ("dK", "dV") else BF16_TOL
         worst = assert_close(to_np(g), r, *tol, f"gqa64 {name}")
-        print(f"gqa64 {name}: {worst}", flush=True)
+        print(f"gqa64 {name}: max |err| {worst:.4f}, required atol at rtol 2e-2 "
+              f"{required_atol(to_np(g), r):.4f} (bound {tol[0]})", flush=True)
     wd = wl.random_workload(35, [1, 1], [5000, 3000], hq, hkv, d, "bf16",
                             wl.MASK_CAUSAL_BOTTOM_RIGHT, name="gqa64-decode")
     print(f"gqa group 64 decode", flush=True)

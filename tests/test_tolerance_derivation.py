@@ -1,50 +1,46 @@
-"""Where the bf16 gradient bound comes from for deep GQA groups (CPU only).
+"""Where the gradient bounds above the standard one come from (CPU only).
 
-dK and dV of a key sum P dO and dS Q over every (query head, query) pair that sees it. The
-backward's contractions take P and dS as bf16 operands and form D = rowsum(dO * O) from the
-bf16 output. Applying exactly those roundings to the fp64 oracle's own values - no kernel
-involved - shows how far they move dK and dV on the 64:1 GQA workload of the GPU limit
-tests, and that a few elements leave 2e-2 + 2e-2 |ref| by the roundings alone. The GPU test
-holds that workload's dK and dV to 8e-2 + 2e-2 |ref|.
+The backward's contractions take P (or, with dropout, Z = P * keep / (1 - p)) and dS as
+bf16 MFMA operands, D = rowsum(dO * O) comes from the bf16 output (an exact D with dropout),
+and dQ, dK, dV are stored as bf16. tests/rounding_model.py applies exactly those roundings to
+exact float64 values. A gradient summed over many large weights (64 query heads over one K/V
+head; 200 queries over 3 keys) then moves beyond 2e-2 + 2e-2 |ref| by these roundings alone,
+while the same model stays inside the standard bound on the other test workloads. Each
+widened bound (gpu_util.GQA64_GRAD_TOL, gpu_util.DROPOUT_GRAD_TOL) is the atol the model
+needs at rtol 2e-2 on exactly the workloads it is applied to, plus 10 %; the GPU tests that
+use them print the kernel's own requirement beside the model's. Bounds follow the pages'
+form by dtype and accumulation ("Attention Algorithm Error and Complexity Tests", second
+section); the widening is the bf16 operand rounding of intermediates, derived here.
 """
 import numpy as np
 
 import oracle
 import workloads as wl
+from gpu_util import DROPOUT_GRAD_TOL, GQA64_GRAD_TOL
+from rounding_model import bf16 as _bf16, model_backward, required_atol
 
 
-def _bf16(x):
-    return wl.round_to_bf16(np.asarray(x, dtype=np.float32)).astype(np.float64)
+def gqa64_workload():
+    """The deep-GQA workload of tests/test_gpu_limits.py::test_gqa_group_of_64."""
+    return wl.random_workload(34, [300, 129], [300, 129], 64, 1, 128, "bf16",
+                              wl.MASK_CAUSAL_TOP_LEFT, with_dout=True, name="gqa64")
 
 
-def test_deep_gqa_gradient_rounding():
-    w = wl.random_workload(34, [300, 129], [300, 129], 64, 1, 128, "bf16",
-                           wl.MASK_CAUSAL_TOP_LEFT, with_dout=True, name="gqa64")
-    q, k, v, do = (np.asarray(a, np.float64) for a in (w.q, w.k, w.v, w.dout))
-    _, rk, rv = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale,
-                                     w.mask_mode)
-    dk = np.zeros_like(rk)
-    dv = np.zeros_like(rv)
-    for s in range(2):
-        a, b = int(w.cu_q[s]), int(w.cu_q[s + 1])
-        n = b - a
-        allowed = np.tril(np.ones((n, n), dtype=bool))  # top-left causal, equal lengths
-        for h in range(64):
-            logits = np.where(allowed, w.scale * q[a:b, h] @ k[a:b, 0].T, -np.inf)
-            p = np.exp(logits - logits.max(axis=1, keepdims=True))
-            p /= p.sum(axis=1, keepdims=True)
-            o = _bf16(p @ v[a:b, 0])                     # the stored output
-            d = (do[a:b, h] * o).sum(axis=1)             # D from the stored output
-            ds = _bf16(p * (do[a:b, h] @ v[a:b, 0].T - d[:, None]))   # bf16 operand
-            dk[a:b, 0] += w.scale * ds.T @ q[a:b, h]
-            dv[a:b, 0] += _bf16(p).T @ do[a:b, h]        # bf16 operand
-    for name, got, ref in (("dK", dk, rk), ("dV", dv, rv)):
-        err = np.abs(got - ref)
-        standard = err > 2e-2 + 2e-2 * np.abs(ref)
-        print(f"{name}: max deviation {err.max():.4f}, {int(standard.sum())} elements beyond "
-              f"2e-2 + 2e-2|ref|")
-        assert standard.any(), f"{name}: the roundings alone stay within the standard bound"
-        assert np.all(err <= 8e-2 + 2e-2 * np.abs(ref)), f"{name}: beyond the deep-GQA bound"
+def test_deep_gqa_gradient_bound_is_derived():
+    """dK and dV of 64 query heads over one K/V head: the model needs atol 0.028 / 0.030 at
+    rtol 2e-2 (beyond the standard 0.02), and its largest absolute deviations, 0.062 (dK)
+    and 0.073 (dV), are the kernel's recorded ones: the stored bf16 outputs of large
+    gradients account for them. dQ needs no widening."""
+    w = gqa64_workload()
+    ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode)
+    got = model_backward(w)
+    need = [required_atol(g, r) for g, r in zip(got, ref)]
+    print(f"gqa64 model: required atol dQ {need[0]:.4f} dK {need[1]:.4f} dV {need[2]:.4f}; "
+          f"max |err| dK {np.abs(got[1] - ref[1]).max():.4f} dV {np.abs(got[2] - ref[2]).max():.4f}")
+    assert need[0] <= 2e-2
+    assert max(need[1], need[2]) > 2e-2, "the standard bound would do"
+    assert max(need[1], need[2]) * 1.1 <= GQA64_GRAD_TOL[0] + 1e-12
+    assert GQA64_GRAD_TOL[0] <= max(need[1], need[2]) * 1.1 + 1e-3, "bound looser than derived"
 
 
 def dropout_backward_workload(d, mode, window):
@@ -85,48 +81,48 @@ def test_dropout_gradients_need_an_exact_d():
     assert beyond["dQ"] > 0 and beyond["dK"] > 0
 
 
-def test_dropout_gradient_operand_rounding():
-    """The dropout backward's contractions take Z = P * keep / (1 - p) (for dV) and dS (for
-    dK and dQ) as bf16 operands, D being exact. Applied alone to the oracle's fp64 values,
-    those roundings move some gradients of the GPU dropout test's workloads beyond
-    2e-2 + 2e-2 |ref|: the sequence of 200 queries over 3 keys sums about 400 rounded
-    weights near 0.4 into every dV entry of its keys. The GPU test holds the dropout
-    gradients to 6e-2 + 2e-2 |ref|, which these roundings stay within."""
-    from oracle.oracle import _softmax_rows
-    p, seed = 0.2, 99
-    thr = oracle.dropout_threshold(p)
-    scale32 = float(np.float32(256.0 / (256 - thr)))
-    beyond, worst = 0, 0.0
+def dropout_canary_workload():
+    """The workload of tests/test_gpu_dropout.py::test_dropout_canaries_no_out_of_bounds_writes."""
+    return wl.random_workload(46, [40, 3, 90], [10, 200, 90], 4, 1, 64, "bf16",
+                              wl.MASK_CAUSAL_BOTTOM_RIGHT, 16, with_dout=True,
+                              name="drop-canary")
+
+
+def test_dropout_gradient_bound_is_derived():
+    """Dropout backward on its ragged edge workloads (p = 0.2, seed 99 as the GPU test): the
+    model with an exact D and bf16 Z and dS needs atol beyond 0.02 (the sequence of 200
+    queries over 3 keys sums about 400 weights near 0.4 into every dV entry of its keys);
+    DROPOUT_GRAD_TOL is that maximum plus 10 %. The canary workload needs less than 0.02
+    and is held to the standard bound."""
+    need = [0.0, 0.0, 0.0]
     for d, mode, window in DROPOUT_CASES:
         w = dropout_backward_workload(d, mode, window)
-        q, k, v, do = (np.asarray(a, np.float64) for a in (w.q, w.k, w.v, w.dout))
         ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, mode, window,
-                                   dropout_p=p, seed=seed)
-        got = [np.zeros_like(x) for x in ref]
-        sq, pq, lq = oracle.token_metadata(w.cu_q)
-        sk, pk, lk = oracle.token_metadata(w.cu_k)
-        for s in range(len(lq)):
-            qa, qb, ka, kb = (int(x) for x in (w.cu_q[s], w.cu_q[s + 1], w.cu_k[s], w.cu_k[s + 1]))
-            if qa == qb or ka == kb:
-                continue
-            a = oracle.allowed(sq[qa:qb, None], pq[qa:qb, None], sk[None, ka:kb],
-                               pk[None, ka:kb], lq[s], lk[s], mode, window)
-            for h in range(4):
-                g = h // 2
-                pr, _ = _softmax_rows(w.scale * q[qa:qb, h] @ k[ka:kb, g].T, a)
-                keep = oracle.dropout_keep(seed, s, h, pq[qa:qb, None], pk[None, ka:kb], thr)
-                zf = np.where(keep, 256.0 / (256 - thr), 0.0)
-                dp = (do[qa:qb, h] @ v[ka:kb, g].T) * zf
-                dd = (pr * dp).sum(axis=1)                                  # exact D
-                ds = _bf16(pr * (dp - dd[:, None]))                         # bf16 operand
-                z = _bf16(np.where(keep, pr * scale32, 0.0))                # bf16 operand
-                got[0][qa:qb, h] = w.scale * ds @ k[ka:kb, g]
-                got[1][ka:kb, g] += w.scale * ds.T @ q[qa:qb, h]
-                got[2][ka:kb, g] += z.T @ do[qa:qb, h]
-        for g_, r_ in zip(got, ref):
-            err = np.abs(g_ - r_)
-            beyond += int(np.sum(err > 2e-2 + 2e-2 * np.abs(r_)))
-            worst = max(worst, float((err / (6e-2 + 2e-2 * np.abs(r_))).max()))
-    print(f"elements beyond the standard bound: {beyond}; worst fraction of the dropout bound: "
-          f"{worst:.2f}")
-    assert beyond > 0 and worst <= 1.0
+                                   dropout_p=0.2, seed=99)
+        got = model_backward(w, 0.2, 99)
+        need = [max(a, required_atol(g, r)) for a, g, r in zip(need, got, ref)]
+    print(f"dropout edges model: required atol dQ {need[0]:.4f} dK {need[1]:.4f} "
+          f"dV {need[2]:.4f}")
+    assert max(need) > 2e-2, "the standard bound would do"
+    assert max(need) * 1.1 <= DROPOUT_GRAD_TOL[0] + 1e-12
+    assert DROPOUT_GRAD_TOL[0] <= max(need) * 1.1 + 1e-3, "bound looser than derived"
+    w = dropout_canary_workload()
+    ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
+                               w.window, dropout_p=0.25, seed=777)
+    got = model_backward(w, 0.25, 777)
+    canary = [required_atol(g, r) for g, r in zip(got, ref)]
+    print(f"dropout canary model: required atol {canary}")
+    assert max(canary) <= 2e-2
+
+
+def test_model_within_standard_bound_on_standard_workloads():
+    """On the backward edge workloads held to the standard bound on the GPU, the model needs
+    no widening either: it does not overstate the operand roundings."""
+    lq = [0, 1, 63, 64, 65, 127, 128, 129, 200, 7]
+    lk = [5, 129, 128, 64, 63, 1, 300, 129, 0, 70]
+    for d, mode, window in ((64, 1, 0), (128, 2, 0), (128, 0, 0), (64, 1, 70)):
+        w = wl.random_workload((21, d, mode), lq, lk, 4, 2, d, "bf16", mode, window,
+                               with_dout=True, name="bwd-edge")
+        ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, mode, window)
+        got = model_backward(w)
+        assert max(required_atol(g, r) for g, r in zip(got, ref)) <= 2e-2, (d, mode, window)
