@@ -9,5 +9,5 @@ from ._binding import (  # noqa: F401
     ATTN_PROBE_PREFILL, ATTN_PROBE_PREFILL_GENERIC, ATTN_PROBE_SPLITK, EXPORTS, AttnError, attn_bwd,
     attn_bwd_dropout, attn_bwd_workspace_size, attn_describe_plan, attn_dropout_probe, attn_fwd,
     attn_fwd_dropout, attn_fwd_dropout_workspace_size, attn_fwd_no_workspace,
-    attn_fwd_workspace_size, attn_mask_probe, attn_mask_probe_ex, attn_status_string, attn_version, library_path,
-    load)
+    attn_fwd_workspace_size, attn_mask_probe, attn_mask_probe_ex, attn_status_string, attn_version,
+    library_path, load, use_library)

@@ -312,7 +312,8 @@ def attn_bwd_dropout(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_se
 
 def attn_dropout_probe(seq, head, q0, nq, k0, nk, dropout_p, seed,
                        device="cuda") -> torch.Tensor:
-    """uint8 [nq, nk]: 1 where the kernels keep element (q0+i, k0+j) of (seq, head)."""
+    """uint8 [nq, nk] for element (q0+i, k0+j) of (seq, head): bit 0 = kept by the row form
+    of the realisation (forward, dQ kernels), bit 1 = kept by the column form (dK/dV)."""
     keep = torch.empty((nq, nk), dtype=torch.uint8, device=device)
     rc = load().attn_dropout_probe(int(seq), int(head), int(q0), int(nq), int(k0), int(nk),
                                    float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF,

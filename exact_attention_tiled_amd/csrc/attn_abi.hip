@@ -500,6 +500,9 @@ int attn_dropout_probe(int32_t seq, int32_t head, int32_t q0, int32_t nq, int32_
                        int32_t nk, float dropout_p, uint64_t seed, uint8_t* keep,
                        void* stream) {
   if (seq < 0 || head < 0 || q0 < 0 || nq < 0 || k0 < 0 || nk < 0) return ATTN_ERR_BAD_RANGE;
+  if ((int64_t)q0 + nq > INT32_MAX - 64 || (int64_t)k0 + nk > INT32_MAX - 64)
+    return ATTN_ERR_BAD_RANGE;
+  if (((q0 + nq + 31) >> 5) - (q0 >> 5) > 65535) return ATTN_ERR_BAD_RANGE;  // grid rows
   uint32_t thr = 0;
   float dscale = 1.0f;
   if (!dropout_threshold(dropout_p, &thr, &dscale)) return ATTN_ERR_BAD_DROPOUT;
@@ -511,6 +514,12 @@ int attn_dropout_probe(int32_t seq, int32_t head, int32_t q0, int32_t nq, int32_
                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
 }
+
+#ifdef ATTN_DEBUG_POISON_LDS
+static const char BUILD_TAG[] = " lds=poisoned";   // race-exposure build
+#else
+static const char BUILD_TAG[] = "";
+#endif
 
 int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
                        int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
@@ -530,17 +539,17 @@ int attn_describe_plan(int32_t num_seqs, int32_t total_q, int32_t total_k, int32
                           max_q, max_k, hq, hkv, d, dtype, 1.0f, mode, window, nullptr, nullptr);
     std::snprintf(buf, len,
                   "path=prefill dtype=%s d=%d tile=%dx%d waves=4 order=%s grid=%d workspace=%zu "
-                  "version=%d",
+                  "version=%d%s",
                   dt, d, attn::FWD_BM, attn::FWD_BN,
                   attn::equal_lengths(a) ? "largest_first" : "cost_sorted",
-                  attn::fwd_prefill_grid(a), plan.workspace, ATTN_VERSION);
+                  attn::fwd_prefill_grid(a), plan.workspace, ATTN_VERSION, BUILD_TAG);
   } else {
     std::snprintf(buf, len,
                   "path=splitk dtype=%s d=%d stage=%d rows_per_kvhead<=%d blocks_per_kvhead=%d "
-                  "chunk=%d partials=%d grid=%ld workspace=%zu version=%d",
+                  "chunk=%d partials=%d grid=%ld workspace=%zu version=%d%s",
                   dt, d, attn::SPLITK_STAGE, (hq / hkv) * max_q, plan.nsb, plan.chunk,
                   plan.nsb * attn::splitk_partials_per_chunk((hq / hkv) * max_q),
-                  (long)num_seqs * hkv * plan.nsb, plan.workspace, ATTN_VERSION);
+                  (long)num_seqs * hkv * plan.nsb, plan.workspace, ATTN_VERSION, BUILD_TAG);
   }
   return ATTN_OK;
 }

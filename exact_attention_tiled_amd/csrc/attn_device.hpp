@@ -323,28 +323,6 @@ __device__ __forceinline__ void dropout_patch(const DropoutSite& d, int qp, int 
   philox4x32_10(w, d.seed_lo, d.seed_hi);
 }
 
-// The 4 keep flags (bit b: key 4 kp + b) of query position pq against keys 4 kp + 0..3.
-__device__ __forceinline__ uint32_t dropout_keep_row(const DropoutSite& d, int pq, int kp) {
-  uint32_t w[4];
-  dropout_patch(d, pq >> 2, kp, w);
-  const uint32_t x = (pq & 2) ? ((pq & 1) ? w[3] : w[2]) : ((pq & 1) ? w[1] : w[0]);
-  uint32_t bits = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) bits |= (((x >> (8 * b)) & 0xFFu) >= d.thr ? 1u : 0u) << b;
-  return bits;
-}
-
-// The 4 keep flags (bit a: query 4 qp + a) of key position pk against queries 4 qp + 0..3.
-__device__ __forceinline__ uint32_t dropout_keep_col(const DropoutSite& d, int qp, int pk) {
-  uint32_t w[4];
-  dropout_patch(d, qp, pk >> 2, w);
-  const int sh = 8 * (pk & 3);
-  uint32_t bits = 0;
-#pragma unroll
-  for (int a = 0; a < 4; ++a) bits |= (((w[a] >> sh) & 0xFFu) >= d.thr ? 1u : 0u) << a;
-  return bits;
-}
-
 // The 4 lanes of an aligned quad share a query quad (forward, dQ) or a key quad (dK/dV), so
 // the 4 patches a quad needs for the 4 register groups of a 32 x 32 block are computed
 // once each: lane c of the quad generates the patch of group c, and every lane fetches the

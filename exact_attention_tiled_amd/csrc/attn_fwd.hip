@@ -996,14 +996,35 @@ __global__ void mask_probe_splitk_kernel(const int32_t* cu_q, const int32_t* cu_
   }
 }
 
-// keep[i * nk + j] = 1 iff element (query position q0 + i, key position k0 + j) of sequence
-// d.s, head d.h survives dropout: the same DropoutSite functions the kernels use.
-__global__ void dropout_probe_kernel(DropoutSite d, int q0, int nq, int k0, int nk,
-                                     uint8_t* keep) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)nq * nk) return;
-  const int i = q0 + (int)(idx / nk), j = k0 + (int)(idx % nk);
-  keep[idx] = (uint8_t)((dropout_keep_row(d, i, j >> 2) >> (j & 3)) & 1u);
+// The dropout realisation as the kernels compute it: one wave per 32 x 32 block of (query,
+// key) positions, both positions 32-aligned as in every kernel's blocks. Row form (forward,
+// dQ): lane l holds query qb + l % 32, register group a the keys kb + 8 a + 4 (l / 32) + 0..3.
+// Column form (dK, dV): lane l holds key kb + l % 32, group a the queries
+// qb + 8 a + 4 (l / 32) + 0..3. keep[i * nk + j] bit 0 is the row form's flag of (q0 + i,
+// k0 + j), bit 1 the column form's.
+__global__ void __launch_bounds__(64) dropout_probe_kernel(DropoutSite d, int q0, int nq,
+                                                           int k0, int nk, uint8_t* keep) {
+  __shared__ uint8_t tile[32][33];
+  const int lane = threadIdx.x, hg = lane >> 5, li = lane & 31;
+  const int qb = (q0 & ~31) + 32 * (int)blockIdx.y, kb = (k0 & ~31) + 32 * (int)blockIdx.x;
+  uint32_t rows[4], cols[4];
+  dropout_keep_rows4(d, qb + li, (kb + 4 * hg) >> 2, rows);
+  dropout_keep_cols4(d, (qb + 4 * hg) >> 2, kb + li, cols);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tile[li][8 * a + 4 * hg + b] = (uint8_t)((rows[a] >> b) & 1u);
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      tile[8 * a + 4 * hg + v][li] |= (uint8_t)(((cols[a] >> v) & 1u) << 1);
+  __syncthreads();
+  for (int e = lane; e < 32 * 32; e += 64) {
+    const int i = qb + (e >> 5) - q0, j = kb + (e & 31) - k0;
+    if (i >= 0 && i < nq && j >= 0 && j < nk) keep[(long)i * nk + j] = tile[e >> 5][e & 31];
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1244,9 +1265,9 @@ hipError_t launch_mask_probe_fwd(const ProbeArgs& a, uint8_t* bits, hipStream_t 
 hipError_t launch_dropout_probe(uint64_t seed, uint32_t thr, int s, int h, int q0, int nq, int k0,
                                 int nk, uint8_t* keep, hipStream_t st) {
   const DropoutSite d{(uint32_t)seed, (uint32_t)(seed >> 32), thr, 1.0f, s, h};
-  const long n = (long)nq * nk;
-  hipLaunchKernelGGL(dropout_probe_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, d,
-                     q0, nq, k0, nk, keep);
+  const dim3 grid((unsigned)(((k0 + nk + 31) >> 5) - (k0 >> 5)),
+                  (unsigned)(((q0 + nq + 31) >> 5) - (q0 >> 5)));
+  hipLaunchKernelGGL(dropout_probe_kernel, grid, dim3(64), 0, st, d, q0, nq, k0, nk, keep);
   return hipGetLastError();
 }
 

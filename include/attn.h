@@ -236,10 +236,17 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* ou
 
 /*
  * attn_dropout_probe - runs the kernels' dropout realisation for sequence index seq and
- * query head head over in-sequence positions [q0, q0 + nq) x [k0, k0 + nk) and writes
- * keep[i * nk + j] = 1 if element (q0 + i, k0 + j) is kept, else 0 (uint8, device memory,
- * nq * nk bytes). Exists so the realisation can be tested bit-exactly. Positions are not
- * checked against any sequence length. Returns ATTN_ERR_BAD_RANGE for negative arguments.
+ * query head head over in-sequence positions [q0, q0 + nq) x [k0, k0 + nk), in the lane
+ * layout the kernels use: 64-lane waves on 32-aligned 32 x 32 blocks, once in the row form
+ * of the forward and dQ kernels (a lane per query, key quads per register group) and once
+ * in the column form of the dK/dV kernel (a lane per key). Writes keep[i * nk + j] (uint8,
+ * device memory, nq * nk bytes): bit 0 = 1 if the row form keeps element (q0 + i, k0 + j),
+ * bit 1 = the same for the column form; bits 2-7 are zero. Both bits agree for a correct
+ * realisation: the flags are a function of logical indices only, so the backward regenerates
+ * the forward's (Causal Mask and Ragged Sequence Layouts, sixth section). Exists so the
+ * realisation can be tested bit-exactly. Positions are not checked against any sequence length. Returns
+ * ATTN_ERR_BAD_RANGE for negative arguments, q0 + nq or k0 + nk beyond 2^31 - 65, or more
+ * than 65535 query blocks of 32.
  */
 int attn_dropout_probe(int32_t seq, int32_t head, int32_t q0, int32_t nq, int32_t k0,
                        int32_t nk, float dropout_p, uint64_t seed, uint8_t* keep,

@@ -129,6 +129,26 @@ def test_describe_plan(lib):
     assert buf.value.startswith(b"path=prefill")
 
 
+def test_race_exposure_library_is_the_poisoned_build(lib):
+    """lib/libattn_poison.so (compiled with ATTN_DEBUG_POISON_LDS) exports the same symbols
+    and says so in its plan description; the release library does not."""
+    if not os.path.exists(eat_build.POISON_LIB_PATH):
+        eat_build.build(poison_lds=True)
+    assert "-DATTN_DEBUG_POISON_LDS" in eat_build.compile_command("/tmp/x.so", poison_lds=True)
+    assert "-DATTN_DEBUG_POISON_LDS" not in eat_build.compile_command("/tmp/x.so")
+    poison = eat.load(eat_build.POISON_LIB_PATH)
+    for n in header_functions():
+        assert hasattr(poison, n), f"{n} missing from libattn_poison.so"
+    buf = ctypes.create_string_buffer(256)
+    for l in (poison, lib):
+        assert l.attn_describe_plan(4, 8192, 8192, 2048, 2048, 16, 16, 128, 0, 1, 0, 0, 0,
+                                    buf, 256) == OK
+        assert buf.value.endswith(b" lds=poisoned") == (l is poison), buf.value
+        assert l.attn_describe_plan(16, 256, 524288, 16, 32768, 32, 8, 128, 0, 2, 0, 0, 0,
+                                    buf, 256) == OK
+        assert buf.value.endswith(b" lds=poisoned") == (l is poison), buf.value
+
+
 def test_build_command_targets_gfx950():
     cmd = eat_build.compile_command("/tmp/x.so")
     assert "--offload-arch=gfx950" in cmd
@@ -163,6 +183,10 @@ def test_dropout_validation(lib):
     assert lib.attn_dropout_probe(0, 0, 0, 4, 0, 4, f(1.0), 1, None, None) == BAD_DROPOUT
     assert lib.attn_dropout_probe(0, 0, 0, 0, 0, 4, f(0.1), 1, None, None) == OK
     assert lib.attn_dropout_probe(0, 0, 0, 4, 0, 4, f(0.1), 1, None, None) == NULL_PTR
+    big = 2**31 - 64
+    assert lib.attn_dropout_probe(0, 0, big, 4, 0, 4, f(0.1), 1, None, None) == BAD_RANGE
+    assert lib.attn_dropout_probe(0, 0, 0, 4, big, 4, f(0.1), 1, None, None) == BAD_RANGE
+    assert lib.attn_dropout_probe(0, 0, 0, 32 * 65536, 0, 1, f(0.1), 1, None, None) == BAD_RANGE
 
 
 def test_no_workspace_validation(lib):

@@ -39,15 +39,21 @@ def bwd_drop(w, t, out, lse, p, seed):
     (2**64 - 1, 0.9, 16383, 31, 131000, 40, 130950, 120),
     (42, 1.0 / 256, 1, 2, 1, 3, 1, 3),
     (42, 255.0 / 256, 1, 2, 0, 16, 0, 16),
+    (7, 0.2, 2, 5, 32, 96, 64, 160),          # several 32-aligned blocks in each direction
+    (99, 0.2, 9, 3, 8160, 64, 256, 64),        # deep in a long sequence, aligned
+    (2**40 + 3, 0.5, 1, 0, 4064, 65, 33, 127),  # ragged tails on both sides
 ])
 def test_dropout_probe_bit_exact(seed, p, seq, head, q0, nq, k0, nk):
-    """The kernels' keep flags equal the oracle's element for element (integer work)."""
+    """The kernels' keep flags, computed in both lane layouts the kernels use (rows of the
+    forward and dQ; columns of dK/dV), equal the oracle's element for element (integer work)."""
     import exact_attention_tiled_amd as eat
-    print(f"dropout probe seed={seed} p={p} seq={seq} head={head}", flush=True)
-    got = eat.attn_dropout_probe(seq, head, q0, nq, k0, nk, p, seed).cpu().numpy().astype(bool)
+    print(f"dropout probe seed={seed} p={p} seq={seq} head={head} q0={q0} k0={k0}", flush=True)
+    got = eat.attn_dropout_probe(seq, head, q0, nq, k0, nk, p, seed).cpu().numpy()
     ref = oracle.dropout_keep(seed, seq, head, np.arange(q0, q0 + nq)[:, None],
                               np.arange(k0, k0 + nk)[None, :], oracle.dropout_threshold(p))
-    assert np.array_equal(got, ref)
+    assert not np.any(got & ~np.uint8(3)), "bits 2-7 must be zero"
+    assert np.array_equal((got & 1).astype(bool), ref), "row form (forward, dQ)"
+    assert np.array_equal((got >> 1 & 1).astype(bool), ref), "column form (dK, dV)"
 
 
 EDGE = [0, 1, 63, 64, 65, 127, 128, 129]
