@@ -12,6 +12,8 @@
 // Main kernel: one workgroup = 8 waves = 128 keys of one (sequence, K/V head), looping
 // over every query head of the group and every 64-query tile that can see those keys (see
 // bwd_main_kernel for the split of work between waves).
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "attn_internal.h"
 
@@ -266,35 +268,43 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
         l4[a] = *reinterpret_cast<const f32x4*>(lse2s + 32 * qh + 8 * a + 4 * hg);
         d4[a] = *reinterpret_cast<const f32x4*>(dvs + 32 * qh + 8 * a + 4 * hg);
       }
-      if constexpr (DROP) {
-        const DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
-        // registers 4a..4a+3 hold queries qa + 8 a + 4 hg + 0..3 against key kj
-        uint32_t keeps[4];
-        dropout_keep_cols4(drop, (qa + 4 * hg) >> 2, kj, keeps);
+      // Weights and dS for MASKED blocks (some pair excluded: the lane test selects) or
+      // full ones (cls == 2: every pair allowed, the test is skipped; a uniform branch
+      // outside the contractions).
+      auto weights = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        if constexpr (DROP) {
+          const DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
+          // registers 4a..4a+3 hold queries qa + 8 a + 4 hg + 0..3 against key kj
+          uint32_t keeps[4];
+          dropout_keep_cols4(drop, (qa + 4 * hg) >> 2, kj, keeps);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint32_t keep = keeps[a];
+          for (int a = 0; a < 4; ++a) {
+            const uint32_t keep = keeps[a];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int r = 4 * a + b;
-            const bool ok = allowed.ok(r);
-            const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[a][b]));
-            const float pv = ok ? e : 0.0f;
-            const bool kept = (keep >> b) & 1u;
-            sacc[r] = kept ? pv * drop.scale : 0.0f;
-            dpacc[r] = pv * ((kept ? dpacc[r] * drop.scale : 0.0f) - d4[a][b]);
+            for (int b = 0; b < 4; ++b) {
+              const int r = 4 * a + b;
+              const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[a][b]));
+              const float pv = (!MASKED || allowed.ok(r)) ? e : 0.0f;
+              const bool kept = (keep >> b) & 1u;
+              sacc[r] = kept ? pv * drop.scale : 0.0f;
+              dpacc[r] = pv * ((kept ? dpacc[r] * drop.scale : 0.0f) - d4[a][b]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[r >> 2][r & 3]));
+            const float pv = (!MASKED || allowed.ok(r)) ? e : 0.0f;
+            sacc[r] = pv;
+            dpacc[r] = pv * (dpacc[r] - d4[r >> 2][r & 3]);
           }
         }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = allowed.ok(r);
-          const float e = fast_exp2(fmaf(sacc[r], p.c, -l4[r >> 2][r & 3]));
-          const float pv = ok ? e : 0.0f;
-          sacc[r] = pv;
-          dpacc[r] = pv * (dpacc[r] - d4[r >> 2][r & 3]);
-        }
-      }
+      };
+      if (cls == 2)
+        weights(std::false_type{});
+      else
+        weights(std::true_type{});
       M::pack_p(sacc, pp[0]);
       M::pack_p(dpacc, pd[0]);
       // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries.
@@ -416,11 +426,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     const int cls = block_class(wp0, wp1, k0, k0 + BN, g, p.mode, p.window);
     if (cls == 0) return;
     const QueryLaneTest allowed(k0, cls, hg, kv_lo, kv_width);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
-      M::qk(sacc, kt + kb * 32 * ROWB, qr, of, lane);
-      M::qk(dpacc, vt + kb * 32 * ROWB, dor, of, lane);
+    // Weights and dS for MASKED blocks (the lane test selects) or full ones (cls == 2: the
+    // test is skipped; a uniform branch outside the contractions).
+    auto weights = [&](auto masked, f32x16& sacc, const f32x16& dpacc, int kb) {
+      constexpr bool MASKED = decltype(masked)::value;
       if constexpr (DROP) {
         const DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
         // registers 4a..4a+3 hold keys k0 + 32 kb + 8 a + 4 hg + 0..3 against query pq
@@ -432,9 +441,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int r = 4 * a + b;
-            const bool ok = allowed.ok(kb, r);
             const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));
-            const float pv = ok ? e : 0.0f;
+            const float pv = (!MASKED || allowed.ok(kb, r)) ? e : 0.0f;
             const float dpz = ((keep >> b) & 1u) ? dpacc[r] * drop.scale : 0.0f;
             if constexpr (DONLY)
               dsum = fmaf(pv, dpz, dsum);
@@ -445,12 +453,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool ok = allowed.ok(kb, r);
           const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));  // computed, then selected
-          const float pv = ok ? e : 0.0f;
+          const float pv = (!MASKED || allowed.ok(kb, r)) ? e : 0.0f;
           sacc[r] = pv * (dpacc[r] - dvl);
         }
       }
+    };
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      M::qk(sacc, kt + kb * 32 * ROWB, qr, of, lane);
+      M::qk(dpacc, vt + kb * 32 * ROWB, dor, of, lane);
+      if (cls == 2)
+        weights(std::false_type{}, sacc, dpacc, kb);
+      else
+        weights(std::true_type{}, sacc, dpacc, kb);
       if constexpr (!DONLY) {
         typename M::PPack pk;
         M::pack_p(sacc, pk);
