@@ -46,10 +46,8 @@ int validate_common(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t 
 int validate_bwd(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
                  int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype, int32_t mode,
                  int32_t window) {
-  const int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype,
-                                 mode, window);
-  if (rc != ATTN_OK) return rc;
-  return dtype == ATTN_BF16 ? ATTN_OK : ATTN_ERR_BAD_DTYPE;
+  return validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                         window);
 }
 
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, 2 other

@@ -74,9 +74,9 @@ __device__ __forceinline__ void visible_queries(int k0, int k1, const SeqGeom& g
 // empty rows mapped to +inf (so every recomputed P of such a row is exactly 0). One wave
 // per (query token, query head).
 // ---------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ out,
-                                                      const __bf16* __restrict__ dout,
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
+                                                      const T* __restrict__ dout,
                                                       const float* __restrict__ lse, int total_q,
                                                       int hq, float* __restrict__ dvec,
                                                       float* __restrict__ lse2) {
@@ -87,11 +87,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   if (item >= (long)total_q * hq) return;
   const int sub = tid % LPR;
   const size_t base = (size_t)item * D + sub * 8;
-  const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + base);
-  const bf16x8 g = *reinterpret_cast<const bf16x8*>(dout + base);
   float acc = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
+  for (int i = 0; i < 8; ++i) acc += (float)out[base + i] * (float)dout[base + i];
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (sub == 0) {
@@ -605,6 +603,227 @@ hipError_t launch_mask_probe_bwd(const ProbeArgs& a, uint8_t* bits, hipStream_t 
 }
 
 // ---------------------------------------------------------------------------------------
+// fp32 backward (v_mfma_f32_32x32x2_f32: exact products, fp32 accumulation), one wave per
+// workgroup. Same arithmetic and mask decisions as the bf16 kernels; tiles are staged in
+// LDS in the fp32 row layout of the forward (Mma<float, D>::at) by plain loads.
+//   bwd_kv_f32_kernel: 32 keys of one (sequence, K/V head); for every query head of the
+//     group and every 32-query block that sees them: S = Q K^T and dP = dO V^T with the
+//     keys on the lanes, P and dS, then dV^T += dO^T P and dK^T += Q^T dS (the forward's
+//     PV contraction over the Q / dO rows).
+//   bwd_dq_f32_kernel: 32 queries of one (sequence, query head); for every 32-key block it
+//     sees: S^T = K Q^T and dP^T = V dO^T with the queries on the lanes, P and dS, then
+//     dQ^T += K^T dS^T.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void stage_rows_f32(char* tile, const float* src, size_t row_stride,
+                                               int rows, int lane) {
+  // rows x D floats from src (row r at src + r * row_stride), zeros past `rows`, into the
+  // swizzled fp32 row layout: lane l copies 16-byte chunks l, l + 64, ...
+  typedef Mma<float, D> M;
+  constexpr int CPR = D / 4;  // 16-byte chunks per row
+  for (int e = lane; e < 32 * CPR; e += 64) {
+    const int r = e / CPR, c = e - r * CPR;
+    const f32x4 x = r < rows ? *reinterpret_cast<const f32x4*>(src + (size_t)r * row_stride + 4 * c)
+                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    *reinterpret_cast<f32x4*>(tile + M::at(r, 4 * c)) = x;
+  }
+}
+
+template <int D, bool DROP>
+__global__ __launch_bounds__(64) void bwd_kv_f32_kernel(BwdParams p) {
+  typedef Mma<float, D> M;
+  constexpr int NDB = D / 32;
+  constexpr int TB = 32 * M::ROWB;  // one 32-row tile
+  __shared__ __attribute__((aligned(256))) char lds[4 * TB + 2 * 32 * 4];
+  char* const kt = lds;
+  char* const vt = lds + TB;
+  char* const qt = lds + 2 * TB;
+  char* const dot = lds + 3 * TB;
+  float* const l2s = reinterpret_cast<float*>(lds + 4 * TB);
+  float* const dvs = l2s + 32;
+  const float* q = reinterpret_cast<const float*>(p.q);
+  const float* k = reinterpret_cast<const float*>(p.k);
+  const float* v = reinterpret_cast<const float*>(p.v);
+  const float* dout = reinterpret_cast<const float*>(p.dout);
+
+  const int lane = threadIdx.x, g = lane >> 5, i = lane & 31;
+  const int kvh = blockIdx.y;
+  // Sequence s owns key-chunk slots floor(cu_k[s] / 32) + s + j, j = its 32-key chunks.
+  const int slot = blockIdx.x;
+  const int s = seq_of_slot<32>(p.cu_k, p.num_seqs, slot);
+  const SeqGeom geo = load_geom(p.cu_q, p.cu_k, s, p.mode);
+  const int j = slot - (geo.k_start / 32 + s);
+  if (j >= (geo.len_k + 31) / 32) return;
+  const int kw0 = 32 * j;  // keys [kw0, kw1) of sequence s
+  const int kw1 = min(kw0 + 32, geo.len_k);
+  const int kj = kw0 + i;
+  const bool kvalid = kj < kw1;
+  int kq_lo, kq_hi;
+  query_interval(kj, geo, p.mode, p.window, kq_lo, kq_hi);
+  const unsigned kq_width = kq_hi > kq_lo ? (unsigned)(kq_hi - kq_lo) : 0u;
+  const size_t krs = (size_t)p.hkv * D, qrs = (size_t)p.hq * D;
+  stage_rows_f32<D>(kt, k + ((size_t)(geo.k_start + kw0) * p.hkv + kvh) * D, krs, kw1 - kw0, lane);
+  stage_rows_f32<D>(vt, v + ((size_t)(geo.k_start + kw0) * p.hkv + kvh) * D, krs, kw1 - kw0, lane);
+
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+  int qlo = 0, qhi = 0;
+  if (kw1 > kw0) visible_queries(kw0, kw1, geo, p.mode, p.window, qlo, qhi);
+  const int qstart = (qlo / 32) * 32;
+  for (int hh = 0; hh < p.group; ++hh) {
+    const int h = kvh * p.group + hh;
+    for (int qa = qstart; qa < qhi; qa += 32) {
+      const int rows = min(32, geo.len_q - qa);
+      __syncthreads();  // the previous block's readers are done
+      stage_rows_f32<D>(qt, q + ((size_t)(geo.q_start + qa) * p.hq + h) * D, qrs, rows, lane);
+      stage_rows_f32<D>(dot, dout + ((size_t)(geo.q_start + qa) * p.hq + h) * D, qrs, rows, lane);
+      if (lane < 32) {
+        const bool ok = lane < rows;
+        const size_t li = (size_t)h * p.total_q + geo.q_start + qa + lane;
+        l2s[lane] = ok ? p.lse2[li] : __builtin_inff();
+        dvs[lane] = ok ? p.dvec[li] : 0.0f;
+      }
+      __syncthreads();
+      const int cls = block_class(qa, qa + rows, kw0, kw0 + 32, geo, p.mode, p.window);
+      if (cls == 0) continue;
+      const KeyLaneTest allowed(qa, cls, g, kq_lo, kq_width);
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll 8
+      for (int st = 0; st < M::QREGS; ++st) {
+        const float qa_ = *reinterpret_cast<const float*>(qt + M::at(i, 2 * st + g));
+        const float ka_ = *reinterpret_cast<const float*>(kt + M::at(i, 2 * st + g));
+        const float da_ = *reinterpret_cast<const float*>(dot + M::at(i, 2 * st + g));
+        const float va_ = *reinterpret_cast<const float*>(vt + M::at(i, 2 * st + g));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa_, ka_, sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x2f32(da_, va_, dpacc, 0, 0, 0);
+      }
+      // register r holds query qa + key_of_reg(r, g) against key kj
+      uint32_t keeps[4] = {0xFu, 0xFu, 0xFu, 0xFu};
+      DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
+      if constexpr (DROP) dropout_keep_cols4(drop, (qa + 4 * g) >> 2, kj, keeps);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = key_of_reg(r, g);
+        const float e = fast_exp2(fmaf(sacc[r], p.c, -l2s[qr]));
+        const float pv = allowed.ok(r) ? e : 0.0f;
+        if constexpr (DROP) {
+          const bool kept = (keeps[r >> 2] >> (r & 3)) & 1u;
+          sacc[r] = kept ? pv * drop.scale : 0.0f;
+          dpacc[r] = pv * ((kept ? dpacc[r] * drop.scale : 0.0f) - dvs[qr]);
+        } else {
+          sacc[r] = pv;
+          dpacc[r] = pv * (dpacc[r] - dvs[qr]);
+        }
+      }
+      typename M::PPack pp, pd;
+      M::pack_p(sacc, pp);
+      M::pack_p(dpacc, pd);
+      M::pv(dva, pp, dot, typename M::Offsets{}, lane);
+      M::pv(dka, pd, qt, typename M::Offsets{}, lane);
+    }
+  }
+  if (kvalid) {
+    float* dkrow = reinterpret_cast<float*>(p.dk) + ((size_t)(geo.k_start + kj) * p.hkv + kvh) * D;
+    float* dvrow = reinterpret_cast<float*>(p.dv) + ((size_t)(geo.k_start + kj) * p.hkv + kvh) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = db * 32 + 8 * a + 4 * g;
+        M::store4(dkrow + d, dka[db][4 * a] * p.scale, dka[db][4 * a + 1] * p.scale,
+                  dka[db][4 * a + 2] * p.scale, dka[db][4 * a + 3] * p.scale);
+        M::store4(dvrow + d, dva[db][4 * a], dva[db][4 * a + 1], dva[db][4 * a + 2], dva[db][4 * a + 3]);
+      }
+  }
+}
+
+template <int D, bool DROP>
+__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdParams p) {
+  typedef Mma<float, D> M;
+  constexpr int NDB = D / 32;
+  constexpr int TB = 32 * M::ROWB;
+  __shared__ __attribute__((aligned(256))) char lds[2 * TB];
+  char* const kt = lds;
+  char* const vt = lds + TB;
+  const float* q = reinterpret_cast<const float*>(p.q);
+  const float* k = reinterpret_cast<const float*>(p.k);
+  const float* v = reinterpret_cast<const float*>(p.v);
+  const float* dout = reinterpret_cast<const float*>(p.dout);
+
+  const int lane = threadIdx.x, g = lane >> 5;
+  const int h = blockIdx.y;
+  // Sequence s owns query-chunk slots floor(cu_q[s] / 32) + s + j.
+  const int slot = blockIdx.x;
+  const int s = seq_of_slot<32>(p.cu_q, p.num_seqs, slot);
+  const SeqGeom geo = load_geom(p.cu_q, p.cu_k, s, p.mode);
+  const int jq = slot - (geo.q_start / 32 + s);
+  if (jq >= (geo.len_q + 31) / 32) return;
+  const int qw0 = 32 * jq;  // queries [qw0, qw1) of sequence s
+  const int qw1 = min(qw0 + 32, geo.len_q);
+  const int pq = qw0 + (lane & 31);
+  const bool qvalid = pq < qw1;
+  const int kvh = h / p.group;
+  typename M::QOperand qr[M::QREGS], dor[M::QREGS];
+  const size_t qoff = ((size_t)(geo.q_start + pq) * p.hq + h) * D;
+  M::load_q(qr, q + qoff, qvalid, false, lane);
+  M::load_q(dor, dout + qoff, qvalid, false, lane);
+  const size_t li = (size_t)h * p.total_q + geo.q_start + pq;
+  const float l2 = qvalid ? p.lse2[li] : __builtin_inff();
+  const float dvl = qvalid ? p.dvec[li] : 0.0f;
+  int kv_lo, kv_hi;
+  key_interval(pq, geo, p.mode, p.window, kv_lo, kv_hi);
+  const unsigned kv_width = kv_hi > kv_lo ? (unsigned)(kv_hi - kv_lo) : 0u;
+  int klo = 0, khi = 0;
+  if (qw1 > qw0) visible_keys(qw0, qw1, geo, p.mode, p.window, klo, khi);
+  const size_t krs = (size_t)p.hkv * D;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  for (int ka = (klo / 32) * 32; ka < khi; ka += 32) {
+    const int rows = min(32, geo.len_k - ka);
+    __syncthreads();
+    stage_rows_f32<D>(kt, k + ((size_t)(geo.k_start + ka) * p.hkv + kvh) * D, krs, rows, lane);
+    stage_rows_f32<D>(vt, v + ((size_t)(geo.k_start + ka) * p.hkv + kvh) * D, krs, rows, lane);
+    __syncthreads();
+    const int cls = block_class(qw0, qw1, ka, ka + 32, geo, p.mode, p.window);
+    if (cls == 0) continue;
+    const QueryLaneTest allowed(ka, cls, g, kv_lo, kv_width);
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    M::qk(sacc, kt, qr, typename M::Offsets{}, lane);
+    M::qk(dpacc, vt, dor, typename M::Offsets{}, lane);
+    uint32_t keeps[4] = {0xFu, 0xFu, 0xFu, 0xFu};
+    DropoutSite drop{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
+    if constexpr (DROP) dropout_keep_rows4(drop, pq, (ka + 4 * g) >> 2, keeps);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(fmaf(sacc[r], p.c, -l2));
+      const float pv = allowed.ok(0, r) ? e : 0.0f;
+      const float dpz =
+          DROP ? (((keeps[r >> 2] >> (r & 3)) & 1u) ? dpacc[r] * drop.scale : 0.0f) : dpacc[r];
+      sacc[r] = pv * (dpz - dvl);
+    }
+    typename M::PPack pk;
+    M::pack_p(sacc, pk);
+    M::pv(acc, pk, kt, typename M::Offsets{}, lane);
+  }
+  if (qvalid) {
+    float* dst = reinterpret_cast<float*>(p.dq) + qoff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = db * 32 + 8 * a + 4 * g;
+        M::store4(dst + d, acc[db][4 * a] * p.scale, acc[db][4 * a + 1] * p.scale,
+                  acc[db][4 * a + 2] * p.scale, acc[db][4 * a + 3] * p.scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------------------
 size_t bwd_workspace_bytes(int total_q, int hq, int d) {
@@ -613,7 +832,7 @@ size_t bwd_workspace_bytes(int total_q, int hq, int d) {
   return 2 * (((vec + 255) / 256) * 256);
 }
 
-template <int D>
+template <typename T, int D>
 static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   const FwdArgs& f = a.f;
   const size_t vecb = (((size_t)f.total_q * f.hq * sizeof(float) + 255) / 256) * 256;
@@ -621,9 +840,9 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   float* lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + vecb);
   const long items = (long)f.total_q * f.hq;
   if (items > 0) {
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((items + 256 / (D / 8) - 1) / (256 / (D / 8)))),
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((items + 256 / (D / 8) - 1) / (256 / (D / 8)))),
                        dim3(256), 0, st,
-                       static_cast<const __bf16*>(a.out), static_cast<const __bf16*>(a.dout), a.lse,
+                       static_cast<const T*>(a.out), static_cast<const T*>(a.dout), a.lse,
                        f.total_q, f.hq, dvec, lse2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -659,6 +878,26 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   p.drop_thr = f.drop_thr;
   p.drop_scale = f.drop_scale;
   p.dvec_out = dvec;
+  if constexpr (std::is_same<T, float>::value) {
+    // fp32: one wave per 32-key / 32-query chunk slot (D = rowsum(dO * O) from the fp32
+    // output is exact enough here: no separate D pass).
+    const int kslots = f.total_k / 32 + f.num_seqs, qslots = f.total_q / 32 + f.num_seqs;
+    if (f.total_k > 0) {
+      if (drop)
+        hipLaunchKernelGGL((bwd_kv_f32_kernel<D, true>), dim3(kslots, f.hkv), dim3(64), 0, st, p);
+      else
+        hipLaunchKernelGGL((bwd_kv_f32_kernel<D, false>), dim3(kslots, f.hkv), dim3(64), 0, st, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (f.total_q > 0) {
+      if (drop)
+        hipLaunchKernelGGL((bwd_dq_f32_kernel<D, true>), dim3(qslots, f.hq), dim3(64), 0, st, p);
+      else
+        hipLaunchKernelGGL((bwd_dq_f32_kernel<D, false>), dim3(qslots, f.hq), dim3(64), 0, st, p);
+    }
+    return hipGetLastError();
+  }
   if (drop && f.total_q > 0) {
     const int grid = ((p.nlogical_q + 7) / 8) * 8;
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3(grid), dim3(256), 0, st, p);
@@ -685,8 +924,9 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, void* ws, hipStream_t st) {
-  if (a.f.dtype != 0) return hipErrorNotSupported;  // the ABI rejects fp32 before this point
-  return a.f.d == 64 ? bwd_typed<64>(a, ws, st) : bwd_typed<128>(a, ws, st);
+  if (a.f.dtype == 0)
+    return a.f.d == 64 ? bwd_typed<__bf16, 64>(a, ws, st) : bwd_typed<__bf16, 128>(a, ws, st);
+  return a.f.d == 64 ? bwd_typed<float, 64>(a, ws, st) : bwd_typed<float, 128>(a, ws, st);
 }
 
 }  // namespace attn

@@ -168,8 +168,8 @@ size_t attn_fwd_ex_workspace_size(int32_t num_seqs, int32_t total_q, int32_t tot
  * outputs for the same inputs and the SAME mask arguments (the backward rebuilds the same
  * logical mask: Causal Mask and Ragged Sequence Layouts, section 6). Keys no query may
  * attend get dk = dv = 0; empty query rows get dq = 0.
- *   dtype            ATTN_BF16 only: an ATTN_F32 call returns ATTN_ERR_BAD_DTYPE before any
- *                    launch, and attn_bwd_workspace_size returns 0 for it
+ *   dtype            ATTN_BF16 or ATTN_F32 (the dtype of q, k, v, out, dout, dq, dk, dv);
+ *                    fp32 products are exact with fp32 accumulation
  *   workspace        device scratch of at least attn_bwd_workspace_size(...) bytes
  *                    (8 * Hq * total_q rounded up to 256-byte pieces); no initialisation needed
  */
@@ -203,9 +203,8 @@ size_t attn_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_
  *               attn_bwd unchanged
  *   seed        any 64-bit value; attn_bwd_dropout must get the forward's dropout_p and seed
  * The forward always runs the prefill path (bf16 or fp32) and needs the workspace of
- * attn_fwd_dropout_workspace_size; the backward is bf16 only like attn_bwd (an ATTN_F32
- * call returns ATTN_ERR_BAD_DTYPE) and needs attn_bwd_workspace_size. Other arguments,
- * ownership and errors as attn_fwd / attn_bwd.
+ * attn_fwd_dropout_workspace_size; the backward (bf16 or fp32, like attn_bwd) needs
+ * attn_bwd_workspace_size. Other arguments, ownership and errors as attn_fwd / attn_bwd.
  */
 int attn_fwd_dropout(const void* q, const void* k, const void* v,
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

@@ -100,16 +100,17 @@ def test_bwd_validation(lib):
     assert need >= 2 * 4 * 2 * 4   # D and LSE (base 2) per (query, head), fp32
 
 
-def test_bwd_rejects_f32_on_the_host(lib):
-    """The backward kernels are bf16 only: fp32 is a validation error returned before any
-    launch (no device is needed to see it), and the size query answers 0 for it."""
-    args = [1] * 8 + [1, 4, 4, 4, 4, 2, 1, 64, 1, ctypes.c_float(0.1), 1, 0, 1, 1, 1, 1, 1 << 20,
+def test_bwd_accepts_both_dtypes(lib):
+    """The backward takes bf16 and fp32 (the workspace size is the same two row vectors);
+    any other dtype code is a validation error returned before any launch."""
+    for dt in (0, 1):
+        assert lib.attn_bwd_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, dt, 1, 0) == 512
+    args = [1] * 8 + [1, 4, 4, 4, 4, 2, 1, 64, 2, ctypes.c_float(0.1), 1, 0, 1, 1, 1, 1, 1 << 20,
                       None]
     assert lib.attn_bwd(*args) == BAD_DTYPE
     dargs = args[:20] + [ctypes.c_float(0.1), ctypes.c_uint64(5)] + args[20:]
     assert lib.attn_bwd_dropout(*dargs) == BAD_DTYPE
-    assert lib.attn_bwd_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 1, 1, 0) == 0
-    assert lib.attn_bwd_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 0, 1, 0) > 0
+    assert lib.attn_bwd_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 2, 1, 0) == 0
 
 
 def test_mask_probe_validation(lib):

@@ -1,4 +1,4 @@
-"""GPU backward parity against the fp64 oracle, GQA group sums, canaries (bf16)."""
+"""GPU backward parity against the fp64 oracle, GQA group sums, canaries (bf16 and fp32)."""
 import numpy as np
 import pytest
 
@@ -135,3 +135,70 @@ def test_train_full_size(window):
         assert_close(gq[rows][:, heads], rq, *BF16_TOL, f"train dQ s{s} g{g}")
         assert_close(gk[krows][:, g], rk, *BF16_TOL, f"train dK s{s} g{g}")
         assert_close(gv[krows][:, g], rv, *BF16_TOL, f"train dV s{s} g{g}")
+
+
+# ----------------------------------------------------------------------------------------
+# fp32 backward (exact products, fp32 accumulation): the fp32 bound 1e-5 + 1e-5 |ref|
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [wl.MASK_CAUSAL_BOTTOM_RIGHT, wl.MASK_NONE])
+def test_bwd_tiny_f32(mode):
+    """The tiny fp32 workload (B=2, H=2, N=128, d=64; bottom-right and noncausal): forward
+    and backward against the oracle at the fp32 bound."""
+    import dataclasses
+    from gpu_util import F32_TOL
+    w = wl.tiny_f32(mode)
+    w = dataclasses.replace(w, dout=np.random.default_rng((1, mode)).standard_normal(
+        w.q.shape, dtype=np.float32))
+    print(f"fp32 tiny backward mode={mode}", flush=True)
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    got = run_bwd(w, t, out, lse)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, _oracle_bwd(w)):
+        assert g.dtype == t["q"].dtype
+        worst = assert_close(to_np(g), r, *F32_TOL, f"fp32 tiny {name}")
+        print(f"fp32 tiny {name}: max abs err {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,window", [(1, 0), (2, 0), (0, 0), (1, 70), (2, 33)])
+def test_bwd_ragged_edges_f32(d, mode, window):
+    """fp32 backward on the ragged edge lengths with GQA 4:2 (dK, dV group sums), every
+    alignment and two windows, at the fp32 bound; keys no query sees get exact zeros."""
+    import torch
+    from gpu_util import F32_TOL
+    lq = [0, 1, 63, 64, 65, 127, 128, 129, 200, 7]
+    lk = [5, 129, 128, 64, 63, 1, 300, 129, 0, 70]
+    w = wl.random_workload((22, d, mode), lq, lk, 4, 2, d, "f32", mode, window,
+                           with_dout=True, name="bwd-edge-f32")
+    print(f"fp32 backward d={d} mode={mode} window={window}", flush=True)
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    dq, dk, dv = run_bwd(w, t, out, lse)
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), _oracle_bwd(w)):
+        assert_close(to_np(g), r, *F32_TOL, f"fp32 edge {name}")
+    m = oracle.explicit_mask(w.cu_q, w.cu_k, w.mask_mode, w.window)
+    unseen = torch.from_numpy(np.nonzero(~m.any(axis=0))[0]).cuda()
+    assert torch.all(dk[unseen] == 0) and torch.all(dv[unseen] == 0)
+
+
+@pytest.mark.parametrize("d,mode,window", [(64, 1, 0), (128, 2, 0), (64, 0, 0), (128, 1, 70)])
+def test_bwd_dropout_edges_f32(d, mode, window):
+    """fp32 dropout backward against the oracle replaying the same realisation, at the fp32
+    bound."""
+    import exact_attention_tiled_amd as eat
+    from gpu_util import F32_TOL
+    edge = [0, 1, 63, 64, 65, 127, 128, 129]
+    w = wl.random_workload((43, d, mode), edge + [5, 200], edge[::-1] + [300, 3], 4, 2, d,
+                           "f32", mode, window, with_dout=True, name="drop-bwd-f32")
+    print(f"fp32 dropout backward d={d} mode={mode} window={window}", flush=True)
+    t = to_device(w)
+    p, seed = 0.2, 99
+    args = (t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+            w.scale, w.mask_mode, w.window)
+    out, lse = eat.attn_fwd_dropout(*args, p, seed)
+    got = eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out, lse, t["dout"], *args[3:], p, seed)
+    ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
+                               w.window, dropout_p=p, seed=seed)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert_close(to_np(g), r, *F32_TOL, f"fp32 dropout {name}")
