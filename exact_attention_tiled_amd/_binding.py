@@ -19,7 +19,7 @@ ATTN_BF16, ATTN_F32 = 0, 1
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL_TOP_LEFT, ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 ATTN_PATH_AUTO, ATTN_PATH_PREFILL, ATTN_PATH_SPLITK = 0, 1, 2
 (ATTN_PROBE_PREFILL, ATTN_PROBE_PREFILL_GENERIC, ATTN_PROBE_SPLITK, ATTN_PROBE_BWD_KV,
- ATTN_PROBE_BWD_Q) = 0, 1, 2, 3, 4
+ ATTN_PROBE_BWD_Q, ATTN_PROBE_BWD_KV_F32, ATTN_PROBE_BWD_Q_F32) = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_ex_workspace_size",
            "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_dropout",

@@ -368,7 +368,7 @@ int attn_mask_probe_ex(const int32_t* cu_q, const int32_t* cu_k, int32_t num_seq
       mode != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
     return ATTN_ERR_BAD_MASK;
   if (window > 0 && mode == ATTN_MASK_NONE) return ATTN_ERR_BAD_MASK;
-  if (unit < ATTN_PROBE_PREFILL || unit > ATTN_PROBE_BWD_Q) return ATTN_ERR_BAD_PLAN;
+  if (unit < ATTN_PROBE_PREFILL || unit > ATTN_PROBE_BWD_Q_F32) return ATTN_ERR_BAD_PLAN;
   if (q0 < 0 || nq < 0 || k0 < 0 || nk < 0 || (long)q0 + nq > total_q || (long)k0 + nk > total_k)
     return ATTN_ERR_BAD_RANGE;
   attn::ProbeArgs a{};

@@ -590,15 +590,77 @@ __global__ void mask_probe_bwd_q_kernel(const int32_t* cu_q, const int32_t* cu_k
   }
 }
 
+// The fp32 kernels' decisions: 32-key chunks against 32-query blocks (dK/dV) and 32-query
+// chunks against 32-key blocks (dQ), one key / query token per wave.
+__global__ void mask_probe_bwd_kv_f32_kernel(const int32_t* cu_q, const int32_t* cu_k,
+                                             int num_seqs, int mode, int window, int q0, int nq,
+                                             int k0, int nk, uint8_t* bits) {
+  const int u = k0 + blockIdx.x, lane = threadIdx.x, hg = lane >> 5;
+  const int s = seq_of_token(cu_k, num_seqs, u);
+  const SeqGeom g = load_geom(cu_q, cu_k, s, mode);
+  const int kj = u - g.k_start;
+  const int kw0 = (kj / 32) * 32, kw1 = min(kw0 + 32, g.len_k);
+  int kq_lo, kq_hi;
+  query_interval(kj, g, mode, window, kq_lo, kq_hi);
+  const unsigned kq_width = kq_hi > kq_lo ? (unsigned)(kq_hi - kq_lo) : 0u;
+  int qlo = 0, qhi = 0;
+  if (kw1 > kw0) visible_queries(kw0, kw1, g, mode, window, qlo, qhi);
+  for (int qa = (qlo / 32) * 32; qa < qhi; qa += 32) {
+    const int rows = min(32, g.len_q - qa);
+    const int cls = block_class(qa, qa + rows, kw0, kw0 + 32, g, mode, window);
+    if (cls == 0) continue;
+    const KeyLaneTest allowed(qa, cls, hg, kq_lo, kq_width);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qp = qa + key_of_reg(r, hg);
+      const int t = g.q_start + qp;
+      if (allowed.ok(r) && qp < g.len_q && t >= q0 && t < q0 + nq)
+        bits[(size_t)(t - q0) * nk + blockIdx.x] = 1;
+    }
+  }
+}
+
+__global__ void mask_probe_bwd_q_f32_kernel(const int32_t* cu_q, const int32_t* cu_k,
+                                            int num_seqs, int mode, int window, int q0, int nq,
+                                            int k0, int nk, uint8_t* bits) {
+  const int t = q0 + blockIdx.x, lane = threadIdx.x, hg = lane >> 5;
+  const int s = seq_of_token(cu_q, num_seqs, t);
+  const SeqGeom g = load_geom(cu_q, cu_k, s, mode);
+  const int pq = t - g.q_start;
+  const int qw0 = (pq / 32) * 32, qw1 = min(qw0 + 32, g.len_q);
+  int kv_lo, kv_hi;
+  key_interval(pq, g, mode, window, kv_lo, kv_hi);
+  const unsigned kv_width = kv_hi > kv_lo ? (unsigned)(kv_hi - kv_lo) : 0u;
+  int klo = 0, khi = 0;
+  if (qw1 > qw0) visible_keys(qw0, qw1, g, mode, window, klo, khi);
+  uint8_t* row = bits + (size_t)blockIdx.x * nk;
+  for (int ka = (klo / 32) * 32; ka < khi; ka += 32) {
+    const int cls = block_class(qw0, qw1, ka, ka + 32, g, mode, window);
+    if (cls == 0) continue;
+    const QueryLaneTest allowed(ka, cls, hg, kv_lo, kv_width);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int u = g.k_start + ka + key_of_reg(r, hg);
+      if (allowed.ok(0, r) && u >= k0 && u < k0 + nk) row[u - k0] = 1;
+    }
+  }
+}
+
 hipError_t launch_mask_probe_bwd(const ProbeArgs& a, uint8_t* bits, hipStream_t st) {
   hipError_t e = launch_probe_zero(bits, (long)a.nq * a.nk, st);
   if (e != hipSuccess || a.nq == 0 || a.nk == 0) return e;
   if (a.unit == 3)
     hipLaunchKernelGGL(mask_probe_bwd_kv_kernel, dim3(a.nk), dim3(64), 0, st, a.cu_q, a.cu_k,
                        a.num_seqs, a.mode, a.window, a.q0, a.nq, a.k0, a.nk, bits);
-  else
+  else if (a.unit == 4)
     hipLaunchKernelGGL(mask_probe_bwd_q_kernel, dim3(a.nq), dim3(64), 0, st, a.cu_q, a.cu_k,
                        a.num_seqs, a.mode, a.window, a.q0, a.nq, a.k0, a.nk, bits);
+  else if (a.unit == 5)
+    hipLaunchKernelGGL(mask_probe_bwd_kv_f32_kernel, dim3(a.nk), dim3(64), 0, st, a.cu_q,
+                       a.cu_k, a.num_seqs, a.mode, a.window, a.q0, a.nq, a.k0, a.nk, bits);
+  else
+    hipLaunchKernelGGL(mask_probe_bwd_q_f32_kernel, dim3(a.nq), dim3(64), 0, st, a.cu_q,
+                       a.cu_k, a.num_seqs, a.mode, a.window, a.q0, a.nq, a.k0, a.nk, bits);
   return hipGetLastError();
 }
 

@@ -273,7 +273,9 @@ enum attn_probe_unit {
   ATTN_PROBE_PREFILL_GENERIC = 1,  /* fp32 prefill and every dropout forward */
   ATTN_PROBE_SPLITK = 2,           /* split-K decode: chunk clip + per-lane test, one head */
   ATTN_PROBE_BWD_KV = 3,           /* backward dK / dV kernel (keys on lanes) */
-  ATTN_PROBE_BWD_Q = 4             /* backward dQ kernel (queries on lanes) */
+  ATTN_PROBE_BWD_Q = 4,            /* backward dQ kernel (queries on lanes) */
+  ATTN_PROBE_BWD_KV_F32 = 5,       /* fp32 backward dK/dV kernel (32-key chunks) */
+  ATTN_PROBE_BWD_Q_F32 = 6         /* fp32 backward dQ kernel (32-query chunks) */
 };
 
 /*

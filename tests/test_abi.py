@@ -221,7 +221,7 @@ def test_mask_probe_ex_validation(lib):
     def call(unit, hq=8, hkv=2, max_q=4, max_k=300, head=0, q0=0, nq=4, k0=0, nk=300):
         return lib.attn_mask_probe_ex(1, 1, 1, 4, 300, max_q, max_k, hq, hkv, 2, 0, unit, head,
                                       0, q0, nq, k0, nk, 1, None)
-    assert call(5) == BAD_PLAN
+    assert call(7) == BAD_PLAN
     assert call(-1) == BAD_PLAN
     assert call(2, hq=32, hkv=1) == BAD_PLAN   # 128 rows per K/V head: prefill only
     assert call(2, head=8) == BAD_RANGE

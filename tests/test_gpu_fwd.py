@@ -38,7 +38,8 @@ MASK_PACKS = [
 ]
 
 
-PROBE_UNITS = {0: "prefill_bf16", 1: "prefill_generic", 3: "bwd_dk_dv", 4: "bwd_dq"}
+PROBE_UNITS = {0: "prefill_bf16", 1: "prefill_generic", 3: "bwd_dk_dv", 4: "bwd_dq",
+               5: "bwd_dk_dv_f32", 6: "bwd_dq_f32"}
 
 
 @pytest.mark.parametrize("unit", sorted(PROBE_UNITS), ids=lambda u: PROBE_UNITS[u])
