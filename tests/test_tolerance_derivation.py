@@ -61,7 +61,8 @@ def test_dropout_gradients_need_an_exact_d():
     a sequence whose 128 queries all see one key has exact dK = 0, yet that D moves it by up
     to 0.13. Shown here from the oracle alone (its backward given its own output rounded to
     bf16). The dropout backward therefore computes D = sum_j P dP in fp32 in a pass of its
-    own, and the GPU dropout test holds every gradient to the standard bound."""
+    own: this shift is then absent, and what the edge gradients still need beyond the
+    standard bound comes from operand roundings alone (DROPOUT_GRAD_TOL, derived below)."""
     p, seed = 0.2, 99
     beyond = {}
     for d, mode, window in DROPOUT_CASES:
