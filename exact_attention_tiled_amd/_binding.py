@@ -25,7 +25,7 @@ EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_ex_wo
            "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_dropout",
            "attn_fwd_dropout_workspace_size", "attn_bwd_dropout", "attn_dropout_probe",
            "attn_mask_probe", "attn_describe_plan", "attn_status_string", "attn_version",
-           "attn_fwd_no_workspace", "attn_mask_probe_ex")
+           "attn_fwd_no_workspace", "attn_mask_probe_ex", "attn_check_seqlens")
 
 _lib = None
 
@@ -82,6 +82,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_dropout.restype = ctypes.c_int
     lib.attn_dropout_probe.argtypes = [_I] * 6 + [_F, _U64, _P, _P]
     lib.attn_dropout_probe.restype = ctypes.c_int
+    lib.attn_check_seqlens.argtypes = [_P, _P] + [_I] * 5 + [_P, _P]
+    lib.attn_check_seqlens.restype = ctypes.c_int
     lib.attn_mask_probe.argtypes = [_P, _P] + [_I] * 9 + [_P, _P]
     lib.attn_mask_probe.restype = ctypes.c_int
     lib.attn_mask_probe_ex.argtypes = [_P, _P] + [_I] * 16 + [_P, _P]
@@ -320,6 +322,25 @@ def attn_dropout_probe(seq, head, q0, nq, k0, nk, dropout_p, seed,
                                    _ptr(keep), _stream())
     _check("attn_dropout_probe", rc)
     return keep
+
+
+SEQLENS_ERRORS = {1: "cu_seqlens_q[0] != 0", 2: "cu_seqlens_q decreases",
+                  4: "cu_seqlens_q[-1] != total_q", 8: "a query length exceeds max_seqlen_q",
+                  16: "cu_seqlens_k[0] != 0", 32: "cu_seqlens_k decreases",
+                  64: "cu_seqlens_k[-1] != total_k", 128: "a key length exceeds max_seqlen_k"}
+
+
+def attn_check_seqlens(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q,
+                       max_seqlen_k) -> int:
+    """The attn_seqlens_error bits of the two arrays (0 = well formed), checked on the device;
+    synchronises the current stream to read the word."""
+    _dev(cu_seqlens_q, cu_seqlens_k)
+    word = torch.empty(1, dtype=torch.int32, device=cu_seqlens_q.device)
+    rc = load().attn_check_seqlens(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                   int(cu_seqlens_q.shape[0]) - 1, int(total_q), int(total_k),
+                                   int(max_seqlen_q), int(max_seqlen_k), _ptr(word), _stream())
+    _check("attn_check_seqlens", rc)
+    return int(word.item())
 
 
 def attn_mask_probe(cu_seqlens_q, cu_seqlens_k, total_q, total_k, mask_mode, window, q0, nq,

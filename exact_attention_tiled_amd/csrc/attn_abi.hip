@@ -513,6 +513,19 @@ int attn_dropout_probe(int32_t seq, int32_t head, int32_t q0, int32_t nq, int32_
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
 }
 
+int attn_check_seqlens(const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs,
+                       int32_t total_q, int32_t total_k, int32_t max_q, int32_t max_k,
+                       int32_t* word, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (!cu_q || !cu_k || !word) return ATTN_ERR_NULL_PTR;
+  int rc = check_device();
+  if (rc != ATTN_OK) return rc;
+  hipError_t e = attn::launch_check_seqlens(cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k,
+                                            word, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
+}
+
 #ifdef ATTN_DEBUG_POISON_LDS
 static const char BUILD_TAG[] = " lds=poisoned";   // race-exposure build
 #else

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "attn.h"
 #include "attn_device.hpp"
 #include "attn_internal.h"
 
@@ -1259,6 +1260,43 @@ hipError_t launch_mask_probe_fwd(const ProbeArgs& a, uint8_t* bits, hipStream_t 
     hipLaunchKernelGGL((mask_probe_splitk_kernel<2>), grid, block, 0, st, a.cu_q, a.cu_k,
                        a.num_seqs, a.mode, a.window, a.group, a.head, a.nsb, a.chunk, a.q0, a.nq,
                        a.k0, a.nk, bits);
+  return hipGetLastError();
+}
+
+// cu_seqlens checks. Thread i looks at sequences i, i + 256, ...; the bits meet in LDS and
+// thread 0 writes the word (always, so the caller's word needs no clearing).
+__global__ __launch_bounds__(256) void check_seqlens_kernel(const int32_t* cu_q,
+                                                            const int32_t* cu_k, int num_seqs,
+                                                            int total_q, int total_k, int max_q,
+                                                            int max_k, int32_t* word) {
+  __shared__ int bits;
+  const int tid = threadIdx.x;
+  if (tid == 0) bits = 0;
+  __syncthreads();
+  int b = 0;
+  for (int s = tid; s < num_seqs; s += blockDim.x) {
+    const long lq = (long)cu_q[s + 1] - cu_q[s], lk = (long)cu_k[s + 1] - cu_k[s];
+    if (lq < 0) b |= ATTN_SEQLENS_Q_DECREASING;
+    if (lq > max_q) b |= ATTN_SEQLENS_Q_ABOVE_MAX;
+    if (lk < 0) b |= ATTN_SEQLENS_K_DECREASING;
+    if (lk > max_k) b |= ATTN_SEQLENS_K_ABOVE_MAX;
+  }
+  if (tid == 0) {
+    if (cu_q[0] != 0) b |= ATTN_SEQLENS_Q_START;
+    if (cu_q[num_seqs] != total_q) b |= ATTN_SEQLENS_Q_END;
+    if (cu_k[0] != 0) b |= ATTN_SEQLENS_K_START;
+    if (cu_k[num_seqs] != total_k) b |= ATTN_SEQLENS_K_END;
+  }
+  if (b != 0) atomicOr(&bits, b);
+  __syncthreads();
+  if (tid == 0) *word = bits;
+}
+
+hipError_t launch_check_seqlens(const int32_t* cu_q, const int32_t* cu_k, int num_seqs,
+                                int total_q, int total_k, int max_q, int max_k, int32_t* word,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(check_seqlens_kernel, dim3(1), dim3(256), 0, st, cu_q, cu_k, num_seqs,
+                     total_q, total_k, max_q, max_k, word);
   return hipGetLastError();
 }
 

@@ -62,10 +62,16 @@ size_t splitk_workspace_bytes(int nsplit_eff, int total_q, int hq, int d);
 hipError_t launch_fwd_splitk(const FwdArgs& a, int blocks_per_kvh, int chunk, void* workspace,
                              hipStream_t stream);
 
+// Well-formedness of cu_seqlens (include/attn.h, attn_check_seqlens): one workgroup ORs the
+// attn_seqlens_error bits of every sequence and writes the word.
+hipError_t launch_check_seqlens(const int32_t* cu_q, const int32_t* cu_k, int num_seqs,
+                                int total_q, int total_k, int max_q, int max_k, int32_t* word,
+                                hipStream_t stream);
+
 // Mask probes (one kernel unit's exclusion decisions replayed into a uint8 [nq, nk] array;
 // include/attn.h, attn_mask_probe_ex). unit: 0 bf16 prefill, 1 generic prefill (fp32,
 // dropout), 2 split-K decode (plan nsb / chunk / nrb, query head `head`), 3 backward dK/dV
-// kernel, 4 backward dQ kernel.
+// kernel, 4 backward dQ kernel, 5 and 6 the same two in fp32.
 struct ProbeArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;

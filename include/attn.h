@@ -41,7 +41,8 @@
  * Errors: every entry point validates its arguments on the host before launching anything
  * and returns ATTN_OK (0) or a negative attn_status; on error no output is written. There
  * is no fallback path: an unsupported combination is an error. Malformed cu_seqlens
- * contents (device memory, not read by the host) are undefined behaviour.
+ * contents (device memory, not read by the host) are undefined behaviour; attn_check_seqlens
+ * detects them.
  */
 #ifndef EXACT_ATTENTION_TILED_ATTN_H
 #define EXACT_ATTENTION_TILED_ATTN_H
@@ -297,6 +298,36 @@ int attn_mask_probe_ex(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                        int32_t mask_mode, int32_t window, int32_t unit, int32_t head,
                        int32_t num_splits, int32_t q0, int32_t nq, int32_t k0, int32_t nk,
                        uint8_t* bits, void* stream);
+
+/*
+ * attn_check_seqlens - checks cu_seqlens_q / cu_seqlens_k on the device against the host
+ * sizes the other entry points are given, and writes one int32 to *error_word (device
+ * memory, caller-owned; asynchronous on stream): 0 if the arrays are well formed, else the
+ * OR of the attn_seqlens_error bits below. The other entry points never read cu_seqlens on
+ * the host and treat malformed contents as undefined behaviour; this is the check a caller
+ * (or a debug path) runs first. The cumulative-length arrays are what locate each
+ * sequence's segment of the packed tensors (Causal Mask and Ragged Sequence Layouts,
+ * section 1), and the same arrays must reach the backward (same page, section 6).
+ *   reads  cu_seqlens_q[0 .. num_seqs], cu_seqlens_k[0 .. num_seqs] (int32, device)
+ *   checks cu[0] == 0, cu[s + 1] >= cu[s], cu[num_seqs] == total, every length <= max_seqlen
+ * Errors (nothing is launched): ATTN_ERR_BAD_SHAPE for negative sizes, ATTN_ERR_NULL_PTR for
+ * a NULL array or word (num_seqs = 0 still reads cu[0] of both arrays).
+ */
+enum attn_seqlens_error {
+  ATTN_SEQLENS_Q_START = 1,        /* cu_seqlens_q[0] != 0 */
+  ATTN_SEQLENS_Q_DECREASING = 2,   /* some cu_seqlens_q[s + 1] < cu_seqlens_q[s] */
+  ATTN_SEQLENS_Q_END = 4,          /* cu_seqlens_q[num_seqs] != total_q */
+  ATTN_SEQLENS_Q_ABOVE_MAX = 8,    /* some query length > max_seqlen_q */
+  ATTN_SEQLENS_K_START = 16,       /* the same four for the keys */
+  ATTN_SEQLENS_K_DECREASING = 32,
+  ATTN_SEQLENS_K_END = 64,
+  ATTN_SEQLENS_K_ABOVE_MAX = 128
+};
+
+int attn_check_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int32_t num_seqs, int32_t total_q, int32_t total_k,
+                       int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t* error_word,
+                       void* stream);
 
 /*
  * attn_describe_plan - writes a one-line description of what attn_fwd_ex would launch for

@@ -228,3 +228,24 @@ def test_mask_probe_ex_validation(lib):
     assert call(0, nq=5) == BAD_RANGE
     assert call(3, k0=1) == BAD_RANGE
     assert call(2, hq=6, hkv=4) == BAD_HEADS
+
+
+def test_check_seqlens_validation(lib):
+    """Negative sizes and NULL arrays or word are refused on the host (nothing launched)."""
+    def call(**kw):
+        a = dict(cu_q=1, cu_k=1, n=1, tq=4, tk=4, mq=4, mk=4, word=1)
+        a.update(kw)
+        return lib.attn_check_seqlens(a["cu_q"], a["cu_k"], a["n"], a["tq"], a["tk"], a["mq"],
+                                      a["mk"], a["word"], None)
+    for k in ("n", "tq", "tk", "mq", "mk"):
+        assert call(**{k: -1}) == BAD_SHAPE, k
+    for k in ("cu_q", "cu_k", "word"):
+        assert call(**{k: None}) == NULL_PTR, k
+
+
+def test_seqlens_error_bits_match_the_header():
+    """The binding's names of the error bits are the header's enum values."""
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    vals = dict(re.findall(r"(ATTN_SEQLENS_\w+) = (\d+)", text))
+    assert sorted(int(v) for v in vals.values()) == sorted(eat.SEQLENS_ERRORS)
+    assert vals["ATTN_SEQLENS_Q_START"] == "1" and vals["ATTN_SEQLENS_K_ABOVE_MAX"] == "128"
