@@ -259,6 +259,9 @@ def bench_train(w, steps, warmup, validate=True, dropout=None):
             eat.attn_fwd_dropout_workspace_size(q, k, cu_q, w.max_seqlen_q, w.max_seqlen_k,
                                                 w.mask_mode, w.window))
     fws = torch.empty(max(fwsb, 1), dtype=torch.uint8, device=dev)
+    # With dropout the forward also hands the backward its output's rounding residual, so
+    # the backward forms D from it instead of recomputing S and dP for D.
+    res = torch.empty_like(q) if dropout is not None else None
 
     def fwd():
         if dropout is None:
@@ -267,7 +270,7 @@ def bench_train(w, steps, warmup, validate=True, dropout=None):
         else:
             eat.attn_fwd_dropout(q, k, v, cu_q, cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale,
                                  w.mask_mode, w.window, dropout[0], dropout[1], out=out,
-                                 lse=lse, workspace=fws)
+                                 lse=lse, workspace=fws, out_residual=res)
 
     def bwd():
         if dropout is None:
@@ -276,7 +279,8 @@ def bench_train(w, steps, warmup, validate=True, dropout=None):
         else:
             eat.attn_bwd_dropout(q, k, v, out, lse, do, cu_q, cu_k, w.max_seqlen_q,
                                  w.max_seqlen_k, w.scale, w.mask_mode, w.window, dropout[0],
-                                 dropout[1], dq=dq, dk=dk, dv=dv, workspace=ws)
+                                 dropout[1], dq=dq, dk=dk, dv=dv, workspace=ws,
+                                 out_residual=res)
 
     def step():
         fwd()

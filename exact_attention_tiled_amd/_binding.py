@@ -73,11 +73,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_workspace_size.argtypes = [_I] * 11
     lib.attn_bwd_workspace_size.restype = _S
     lib.attn_fwd_dropout.argtypes = [_P, _P, _P, _P, _P] + [_I] * 9 + [_F, _I, _I, _F, _U64,
-                                                                       _P, _P, _P, _S, _P]
+                                                                       _P, _P, _P, _P, _S, _P]
     lib.attn_fwd_dropout.restype = ctypes.c_int
     lib.attn_fwd_dropout_workspace_size.argtypes = [_I] * 11
     lib.attn_fwd_dropout_workspace_size.restype = _S
-    lib.attn_bwd_dropout.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P] + [_I] * 9 + \
+    lib.attn_bwd_dropout.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P] + [_I] * 9 + \
         [_F, _I, _I, _F, _U64, _P, _P, _P, _P, _S, _P]
     lib.attn_bwd_dropout.restype = ctypes.c_int
     lib.attn_dropout_probe.argtypes = [_I] * 6 + [_F, _U64, _P, _P]
@@ -263,10 +263,12 @@ def attn_fwd_dropout_workspace_size(q, k, cu_q, max_seqlen_q, max_seqlen_k, mask
 
 
 def attn_fwd_dropout(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
-                     mask_mode, window, dropout_p, seed, *, out=None, lse=None, workspace=None):
+                     mask_mode, window, dropout_p, seed, *, out=None, lse=None, workspace=None,
+                     out_residual=None):
     """Forward with dropout on the attention weights (attn_fwd_dropout in include/attn.h):
-    returns (out, lse); lse is that of the undropped softmax."""
-    _dev(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, workspace)
+    returns (out, lse); lse is that of the undropped softmax. A bf16 `out_residual` tensor
+    shaped like q receives each output's rounding residual, for attn_bwd_dropout."""
+    _dev(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, workspace, out_residual)
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -284,16 +286,19 @@ def attn_fwd_dropout(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seql
                                  _ptr(cu_seqlens_k), n, tq, tk, mq, mk, hq, hkv, d,
                                  _dtype_code(q), float(scale), int(mask_mode), int(window),
                                  float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out),
-                                 _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream())
+                                 _ptr(lse), _ptr(out_residual), _ptr(workspace),
+                                 int(workspace.numel()), _stream())
     _check("attn_fwd_dropout", rc)
     return out, lse
 
 
 def attn_bwd_dropout(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                      max_seqlen_k, scale, mask_mode, window, dropout_p, seed, *, dq=None,
-                     dk=None, dv=None, workspace=None):
-    """Backward of attn_fwd_dropout with the same dropout_p and seed; returns (dq, dk, dv)."""
-    _dev(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace)
+                     dk=None, dv=None, workspace=None, out_residual=None):
+    """Backward of attn_fwd_dropout with the same dropout_p and seed; returns (dq, dk, dv).
+    With the forward's `out_residual` the separate pass that computes D is skipped."""
+    _dev(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace,
+         out_residual)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -302,7 +307,8 @@ def attn_bwd_dropout(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_se
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     n, tq, tk, mq, mk, hq, hkv, d = _shape_args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k)
-    rc = load().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+    rc = load().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _ptr(out_residual), _ptr(dout),
                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), n, tq, tk, mq, mk, hq,
                                  hkv, d, _dtype_code(q), float(scale), int(mask_mode),
                                  int(window), float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF,

@@ -426,11 +426,12 @@ int attn_fwd_dropout(const void* q, const void* k, const void* v, const int32_t*
                      const int32_t* cu_k, int32_t num_seqs, int32_t total_q, int32_t total_k,
                      int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d,
                      int32_t dtype, float scale, int32_t mode, int32_t window, float dropout_p,
-                     uint64_t seed, void* out, float* lse, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     uint64_t seed, void* out, float* lse, void* out_residual,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
                            window);
   if (rc != ATTN_OK) return rc;
+  if (out_residual != nullptr && dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   uint32_t thr = 0;
   float dscale = 1.0f;
@@ -451,12 +452,14 @@ int attn_fwd_dropout(const void* q, const void* k, const void* v, const int32_t*
   a.drop_thr = thr;
   a.drop_scale = dscale;
   a.seed = seed;
+  a.out_res = out_residual;
   hipError_t e = attn::launch_fwd_prefill(a, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH_FAILED;
 }
 
 int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out,
-                     const float* lse, const void* dout, const int32_t* cu_q, const int32_t* cu_k,
+                     const float* lse, const void* out_residual, const void* dout,
+                     const int32_t* cu_q, const int32_t* cu_k,
                      int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
                      int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
                      float scale, int32_t mode, int32_t window, float dropout_p, uint64_t seed,
@@ -465,6 +468,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* ou
   int rc = validate_bwd(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
                         window);
   if (rc != ATTN_OK) return rc;
+  if (out_residual != nullptr && dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   uint32_t thr = 0;
   float dscale = 1.0f;
@@ -485,6 +489,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* ou
   a.f.drop_scale = dscale;
   a.f.seed = seed;
   a.out = out;
+  a.out_res = thr > 0 ? out_residual : nullptr;
   a.lse = lse;
   a.dout = dout;
   a.dq = dq;

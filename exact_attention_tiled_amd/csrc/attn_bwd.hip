@@ -76,11 +76,13 @@ __device__ __forceinline__ void visible_queries(int k0, int k1, const SeqGeom& g
 // ---------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
+                                                      const T* __restrict__ out_res,
                                                       const T* __restrict__ dout,
                                                       const float* __restrict__ lse, int total_q,
                                                       int hq, float* __restrict__ dvec,
                                                       float* __restrict__ lse2) {
-  // D / 8 lanes per (token, head) row, 16 bytes of O and dO each.
+  // D / 8 lanes per (token, head) row, 16 bytes of O and dO each. With out_res (bf16
+  // dropout), O is the stored output plus its rounding residual.
   constexpr int LPR = D / 8;
   const int tid = threadIdx.x;
   const long item = (long)blockIdx.x * (256 / LPR) + tid / LPR;
@@ -88,8 +90,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
   const int sub = tid % LPR;
   const size_t base = (size_t)item * D + sub * 8;
   float acc = 0.0f;
+  if (out_res != nullptr) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc += (float)out[base + i] * (float)dout[base + i];
+    for (int i = 0; i < 8; ++i)
+      acc += ((float)out[base + i] + (float)out_res[base + i]) * (float)dout[base + i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += (float)out[base + i] * (float)dout[base + i];
+  }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (sub == 0) {
@@ -904,8 +912,8 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   if (items > 0) {
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((items + 256 / (D / 8) - 1) / (256 / (D / 8)))),
                        dim3(256), 0, st,
-                       static_cast<const T*>(a.out), static_cast<const T*>(a.dout), a.lse,
-                       f.total_q, f.hq, dvec, lse2);
+                       static_cast<const T*>(a.out), static_cast<const T*>(a.out_res),
+                       static_cast<const T*>(a.dout), a.lse, f.total_q, f.hq, dvec, lse2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -960,7 +968,9 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  if (drop && f.total_q > 0) {
+  // Dropout: D = sum_j P dP needs the unrounded output. With the forward's residual the
+  // preprocess above already formed it; otherwise a pass of its own computes it exactly.
+  if (drop && a.out_res == nullptr && f.total_q > 0) {
     const int grid = ((p.nlogical_q + 7) / 8) * 8;
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3(grid), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();

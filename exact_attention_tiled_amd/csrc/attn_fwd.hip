@@ -42,6 +42,7 @@ struct FwdParams {
   // dropout (prefill kernel instantiated with DROP only)
   uint32_t seed_lo, seed_hi, drop_thr;
   float drop_scale;
+  __bf16* out_res;  // bf16 with DROP: rounding residual of O (null = not wanted)
 };
 
 // The exponent offset of a row moves only when a tile's maximum exceeds it by more than
@@ -57,13 +58,16 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 // m_run is in log2 units of the scaled logits; l_run is this lane's partial denominator
 // (the other half of the row lives in lane l ^ 32).
 // With DROP the denominator still sums every weight, and the PV operand carries
-// weight * keep / (1 - p) (the keep flags of DropoutSite for this lane's query).
-template <typename M, int NK, int D, bool DROP = false>
+// weight * keep / (1 - p) (the keep flags of DropoutSite for this lane's query). With RES
+// (bf16) that operand z is also split: pk gets bf16(z) and pkr bf16(z - bf16(z)), so that
+// accumulating both against V gives the unrounded output to about 2^-16.
+template <typename M, int NK, int D, bool DROP = false, bool RES = false>
 __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack (&pk)[NK],
                                              bool need_mask, int pq, int kpos0, const SeqGeom& g,
                                              int mode, int window, float c2, float& m_run,
                                              float& l_run, f32x16 (&o)[D / 32], int lane,
-                                             const DropoutSite& drop = DropoutSite{}) {
+                                             const DropoutSite& drop = DropoutSite{},
+                                             typename M::PPack* pkr = nullptr) {
   if (need_mask) mask_blocks<NK>(s, pq, kpos0, g, mode, window, lane);
   float mx = neg_inf();
 #pragma unroll
@@ -114,6 +118,12 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack 
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           s[kb][4 * a + b] = ((keep[a] >> b) & 1u) ? s[kb][4 * a + b] * drop.scale : 0.0f;
+      if constexpr (RES) {
+        f32x16 lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lo[r] = s[kb][r] - (float)(__bf16)s[kb][r];
+        (void)M::pack_p(lo, pkr[kb]);
+      }
       (void)M::pack_p(s[kb], pk[kb]);
     }
   } else {
@@ -172,7 +182,8 @@ __device__ __forceinline__ bool prefill_tile(const FwdParams& p, int& h, int& s,
 }
 
 // Running state of one prefill wave (32 query rows) and its step over one 64-key stage.
-template <typename T, int D, bool DROP = false>
+// RES (bf16 with DROP): the weights also go through V as their bf16 residuals.
+template <typename T, int D, bool DROP = false, bool RES = false>
 struct PrefillWave {
   typedef Mma<T, D> M;
   f32x16 o[D / 32];
@@ -212,12 +223,13 @@ struct PrefillWave {
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    typename M::PPack pk[2];
-    softmax_step<M, 2, D, DROP>(sacc, pk, cls == 1, pq, k0, g, p.mode, p.window, p.c2, m_run,
-                                l_run, o, lane, drop);
+    typename M::PPack pk[2], pkr[2];  // pkr: RES only
+    softmax_step<M, 2, D, DROP, RES>(sacc, pk, cls == 1, pq, k0, g, p.mode, p.window, p.c2,
+                                     m_run, l_run, o, lane, drop, pkr);
     __builtin_amdgcn_s_setprio(1);
     if constexpr (std::is_same<T, __bf16>::value) {
       M::pv2(o, pk, vt, of);
+      if constexpr (RES) M::pv2(o, pkr, vt, of);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) M::pv(o, pk[kb], vt + kb * 32 * ROWB, of, lane);
@@ -262,8 +274,9 @@ struct PrefillVStage<__bf16, D> {
 // ---------------------------------------------------------------------------------------
 // With DROP the weights reaching V carry the dropout realisation (DropoutSite); this
 // kernel is the forward of every dropout call.
-template <typename T, int D, bool DROP = false>
+template <typename T, int D, bool DROP = false, bool RES = false>
 __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
+  static_assert(!RES || (DROP && std::is_same<T, __bf16>::value), "residual: bf16 dropout");
   typedef Mma<T, D> M;
   constexpr int BM = FWD_BM, BN = FWD_BN, ROWB = M::ROWB;
   constexpr int KTILE = BN * ROWB, VTILE = PrefillVStage<T, D>::TILE_BYTES;
@@ -302,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
   PrefillVStage<T, D> vst;
   vst.init(wave, lane, tid, rstride);
 
-  PrefillWave<T, D, DROP> st;
+  PrefillWave<T, D, DROP, RES> st;
   st.init();
   DropoutSite drop{};
   if constexpr (DROP) drop = DropoutSite{p.seed_lo, p.seed_hi, p.drop_thr, p.drop_scale, s, h};
@@ -357,6 +370,25 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
                   nonempty ? o[db][4 * a + 1] * inv : 0.0f, nonempty ? o[db][4 * a + 2] * inv : 0.0f,
                   nonempty ? o[db][4 * a + 3] * inv : 0.0f);
       }
+    if constexpr (RES) {
+      // The residual x - bf16(x) of every stored element (bf16, |r| <= half an ulp of the
+      // output), so that the backward can form D = rowsum(dO * O) from the unrounded O.
+      {
+        __bf16* rrow = p.out_res + ((size_t)(g.q_start + pq) * p.hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float y = nonempty ? o[db][4 * a + e] * inv : 0.0f;
+              x[e] = y - (float)(__bf16)y;
+            }
+            M::store4(rrow + db * 32 + 8 * a + 4 * hg, x[0], x[1], x[2], x[3]);
+          }
+      }
+    }
     if (hg == 0)
       p.lse[(size_t)h * p.total_q + g.q_start + pq] =
           nonempty ? (m_run + fast_log2(lt)) * LN2 : neg_inf();
@@ -1180,6 +1212,14 @@ static hipError_t prefill_typed(const FwdArgs& a, void* ws, hipStream_t st) {
     p.seed_hi = (uint32_t)(a.seed >> 32);
     p.drop_thr = a.drop_thr;
     p.drop_scale = a.drop_scale;
+    p.out_res = static_cast<__bf16*>(a.out_res);
+    if constexpr (std::is_same<T, __bf16>::value) {
+      if (p.out_res != nullptr) {
+        hipLaunchKernelGGL((fwd_prefill_kernel<T, D, true, true>), dim3(grid), dim3(256), 0, st,
+                           p);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((fwd_prefill_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
   } else if constexpr (std::is_same<T, __bf16>::value) {
     hipLaunchKernelGGL((fwd_prefill_bf16_kernel<D>), dim3(grid), dim3(256), 0, st, p);

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 100   /* 1.0.0 */
+#define ATTN_VERSION 110   /* 1.1.0 */
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -206,6 +206,14 @@ size_t attn_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_
  * The forward always runs the prefill path (bf16 or fp32) and needs the workspace of
  * attn_fwd_dropout_workspace_size; the backward (bf16 or fp32, like attn_bwd) needs
  * attn_bwd_workspace_size. Other arguments, ownership and errors as attn_fwd / attn_bwd.
+ *   out_residual  optional (may be NULL), bf16 only (ATTN_ERR_BAD_DTYPE otherwise), used
+ *               only when t8 > 0: [total_q, Hq, head_dim] bf16 like out. The forward writes
+ *               x - bf16(x) for every output element x it rounds into out; given the same
+ *               buffer, the backward forms D = rowsum(dO * O) from out + out_residual.
+ *               Without it the bf16 backward computes D = sum_u P dP in a pass of its own
+ *               (the stored output's rounding no longer cancels in dS once weights are
+ *               dropped and rescaled), which costs a recomputation of S and dP; the residual
+ *               trades that pass for one more output-sized tensor kept from the forward.
  */
 int attn_fwd_dropout(const void* q, const void* k, const void* v,
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -214,8 +222,8 @@ int attn_fwd_dropout(const void* q, const void* k, const void* v,
                      int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t dtype,
                      float scale, int32_t mask_mode, int32_t window,
                      float dropout_p, uint64_t seed,
-                     void* out, float* lse, void* workspace, size_t workspace_bytes,
-                     void* stream);
+                     void* out, float* lse, void* out_residual, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 size_t attn_fwd_dropout_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k,
                                        int32_t max_seqlen_q, int32_t max_seqlen_k,
@@ -224,7 +232,7 @@ size_t attn_fwd_dropout_workspace_size(int32_t num_seqs, int32_t total_q, int32_
                                        int32_t window);
 
 int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out,
-                     const float* lse, const void* dout,
+                     const float* lse, const void* out_residual, const void* dout,
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                      int32_t num_seqs, int32_t total_q, int32_t total_k,
                      int32_t max_seqlen_q, int32_t max_seqlen_k,

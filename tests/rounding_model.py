@@ -36,8 +36,12 @@ def required_atol(got, ref):
     return float(max(0.0, (err - RTOL * np.abs(ref)).max())) if err.size else 0.0
 
 
-def model_backward(w, dropout_p=0.0, seed=0):
-    """(dQ, dK, dV) of the rounding model for workload w (bf16 inputs, any mask, GQA)."""
+def model_backward(w, dropout_p=0.0, seed=0, residual=False):
+    """(dQ, dK, dV) of the rounding model for workload w (bf16 inputs, any mask, GQA). With
+    dropout, D is exact, or with residual=True formed from the stored output plus its bf16
+    rounding residual; the forward that writes the residual splits each weight Z into
+    bf16(Z) + bf16(Z - bf16(Z)) and accumulates both against V, so its unrounded output is
+    the exact one to about 2^-16."""
     q, k, v, do = (np.asarray(a, np.float64) for a in (w.q, w.k, w.v, w.dout))
     thr = oracle.dropout_threshold(dropout_p)
     zscale = float(np.float32(256.0 / (256 - thr))) if thr > 0 else 1.0
@@ -69,7 +73,13 @@ def model_backward(w, dropout_p=0.0, seed=0):
             else:
                 zf = 1.0
             dp = (do[qa:qb, h] @ v[ka:kb, g].T) * zf
-            if thr > 0:
+            if thr > 0 and residual:
+                z_hi = bf16(pt * zf)
+                z_lo = bf16(pt * zf - z_hi)
+                of = (z_hi @ v[ka:kb, g] + z_lo @ v[ka:kb, g]) / l1   # the forward's fp32 O
+                o = bf16(of) + bf16(of - bf16(of))              # stored output + residual
+                dd = (do[qa:qb, h] * o).sum(axis=1)
+            elif thr > 0:
                 dd = (p * dp).sum(axis=1)                       # the dropout path's exact D
             else:
                 o = bf16((bf16(pt) @ v[ka:kb, g]) / l1)        # the stored forward output

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert eat.attn_version() == 100
+    assert eat.attn_version() == 110
     for code in (OK, NULL_PTR, BAD_SHAPE, BAD_HEADS, BAD_DTYPE, BAD_MASK, WS_SMALL, -7, -8,
                  BAD_SCALE, BAD_PLAN, BAD_RANGE, BAD_DROPOUT, SCRATCH_SMALL):
         s = eat.attn_status_string(code)
@@ -108,7 +108,11 @@ def test_bwd_accepts_both_dtypes(lib):
     args = [1] * 8 + [1, 4, 4, 4, 4, 2, 1, 64, 2, ctypes.c_float(0.1), 1, 0, 1, 1, 1, 1, 1 << 20,
                       None]
     assert lib.attn_bwd(*args) == BAD_DTYPE
-    dargs = args[:20] + [ctypes.c_float(0.1), ctypes.c_uint64(5)] + args[20:]
+    dargs = args[:5] + [None] + args[5:20] + [ctypes.c_float(0.1), ctypes.c_uint64(5)] + args[20:]
+    assert lib.attn_bwd_dropout(*dargs) == BAD_DTYPE
+    # the output residual exists for bf16 only
+    dargs[17] = 1      # dtype ATTN_F32
+    dargs[5] = 1       # out_residual
     assert lib.attn_bwd_dropout(*dargs) == BAD_DTYPE
     assert lib.attn_bwd_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 2, 1, 0) == 0
 
@@ -162,21 +166,23 @@ def test_dropout_validation(lib):
     f = ctypes.c_float
 
     def fwd(p, **kw):
-        a = dict(q=1, k=1, v=1, cu_q=1, cu_k=1, d=64, out=1, lse=1, ws=None, wsb=0)
+        a = dict(q=1, k=1, v=1, cu_q=1, cu_k=1, d=64, dtype=0, out=1, lse=1, res=None, ws=None,
+                 wsb=0)
         a.update(kw)
         return lib.attn_fwd_dropout(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], 1, 4, 4, 4, 4,
-                                    2, 1, a["d"], 0, f(0.125), 1, 0, f(p), 12345, a["out"],
-                                    a["lse"], a["ws"], a["wsb"], None)
+                                    2, 1, a["d"], a["dtype"], f(0.125), 1, 0, f(p), 12345,
+                                    a["out"], a["lse"], a["res"], a["ws"], a["wsb"], None)
 
     for p in (1.0, -0.1, 255.6 / 256, float("nan"), float("inf")):
         assert fwd(p) == BAD_DROPOUT, p
     assert fwd(0.1, d=96) == BAD_SHAPE
     assert fwd(0.1, out=None) == NULL_PTR
-    bargs = [1] * 8 + [1, 4, 4, 4, 4, 2, 1, 64, 0, f(0.1), 1, 0, f(1.5), 7, 1, 1, 1, None, 0,
+    assert fwd(0.1, dtype=1, res=1) == BAD_DTYPE   # residual: bf16 only
+    bargs = [1] * 9 + [1, 4, 4, 4, 4, 2, 1, 64, 0, f(0.1), 1, 0, f(1.5), 7, 1, 1, 1, None, 0,
                        None]
     assert lib.attn_bwd_dropout(*bargs) == BAD_DROPOUT
-    bargs[20] = f(0.2)
-    bargs[23] = None   # dk
+    bargs[21] = f(0.2)
+    bargs[24] = None   # dk
     assert lib.attn_bwd_dropout(*bargs) == NULL_PTR
     assert lib.attn_fwd_dropout_workspace_size(1, 4, 4, 4, 4, 2, 1, 64, 0, 1, 0) == 0
     assert lib.attn_fwd_dropout_workspace_size(2, 9, 9, 5, 5, 2, 1, 64, 0, 1, 0) > 0  # ragged

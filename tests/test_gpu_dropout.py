@@ -20,17 +20,24 @@ def _lib():
     eat.load()
 
 
-def fwd_drop(w, t, p, seed):
+def fwd_drop(w, t, p, seed, res=None):
     import exact_attention_tiled_amd as eat
     return eat.attn_fwd_dropout(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q,
-                                w.max_seqlen_k, w.scale, w.mask_mode, w.window, p, seed)
+                                w.max_seqlen_k, w.scale, w.mask_mode, w.window, p, seed,
+                                out_residual=res)
 
 
-def bwd_drop(w, t, out, lse, p, seed):
+def bwd_drop(w, t, out, lse, p, seed, res=None):
     import exact_attention_tiled_amd as eat
     return eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out, lse, t["dout"], t["cu_q"],
                                 t["cu_k"], w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
-                                w.window, p, seed)
+                                w.window, p, seed, out_residual=res)
+
+
+def residual_buffer(t):
+    """Output-residual buffer of the bf16 dropout forward (None: no residual)."""
+    import torch
+    return torch.full_like(t["q"], float("nan"))
 
 
 @pytest.mark.parametrize("seed,p,seq,head,q0,nq,k0,nk", [
@@ -88,10 +95,12 @@ def test_dropout_forward_edges(dtype, d, mode, window):
         assert_close(to_np(lse), rl, LSE_TOL, 0.0, f"dropout LSE p={p}")
 
 
+@pytest.mark.parametrize("residual", [False, True], ids=["exact_d_pass", "residual"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mode,window", [(1, 0), (2, 0), (0, 0), (1, 70)])
-def test_dropout_backward_edges(d, mode, window):
-    """dQ, dK, dV (GQA group sums) against the oracle replaying the forward's realisation."""
+def test_dropout_backward_edges(d, mode, window, residual):
+    """dQ, dK, dV (GQA group sums) against the oracle replaying the forward's realisation,
+    with D from the backward's own pass or from the forward's output plus its residual."""
     lq = EDGE + [5, 200]
     lk = EDGE[::-1] + [300, 3]
     # N(0,1) values: the backward forms D = rowsum(dO * O) from the stored bf16 output, so
@@ -99,17 +108,52 @@ def test_dropout_backward_edges(d, mode, window):
     # 0.5 near |O| = 90) far above the gradient tolerance.
     w = wl.random_workload((42, d, mode), lq, lk, 4, 2, d, "bf16", mode, window,
                            with_dout=True, name="drop-bwd")
-    print(f"dropout bwd d={d} mode={mode} window={window}", flush=True)
+    print(f"dropout bwd d={d} mode={mode} window={window} residual={residual}", flush=True)
     t = to_device(w)
     p, seed = 0.2, 99
-    out, lse = fwd_drop(w, t, p, seed)
-    got = bwd_drop(w, t, out, lse, p, seed)
+    res = residual_buffer(t) if residual else None
+    out, lse = fwd_drop(w, t, p, seed, res)
+    got = bwd_drop(w, t, out, lse, p, seed, res)
     ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
                                w.window, dropout_p=p, seed=seed)
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         worst = assert_close(to_np(g), r, *DROPOUT_GRAD_TOL, f"dropout {name}")
         print(f"dropout {name}: max |err| {worst:.4f}, required atol at rtol 2e-2 "
               f"{required_atol(to_np(g), r):.4f} (bound {DROPOUT_GRAD_TOL[0]})", flush=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,window", [(1, 0), (2, 0), (0, 0), (2, 70)])
+def test_dropout_output_residual(d, mode, window):
+    """The forward's output residual: out + residual is the unrounded output (within 1e-4 +
+    1e-4 |ref| of the oracle, against 2e-2 for out alone), the residual is at most half a
+    bf16 spacing of out (out is the nearest bf16 to out + residual, up to a tie made by the
+    residual's own rounding), and rows with no allowed key have +0.0 in both."""
+    import torch
+    lq = EDGE + [5, 200]
+    lk = EDGE[::-1] + [300, 3]
+    w = wl.random_workload((41, d, mode), lq, lk, 4, 2, d, "bf16", mode, window,
+                           name="drop-edge", v_offsets=True)
+    print(f"dropout residual d={d} mode={mode} window={window}", flush=True)
+    t = to_device(w)
+    res = residual_buffer(t)
+    out, lse = fwd_drop(w, t, 0.1, 7, res)
+    ro, _ = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode, w.window,
+                             dropout_p=0.1, seed=7)
+    o, r = to_np(out), to_np(res)
+    assert np.all(np.isfinite(r))
+    assert_close(o, ro, *BF16_TOL, "dropout O (rounded)")
+    assert_close(o.astype(np.float64) + r, ro, 1e-4, 1e-4, "dropout O + residual")
+    # spacing above |out|: the next bf16 magnitude minus |out| (the spacing below is never
+    # larger, so |residual| <= half of it on both sides)
+    mag = out.view(torch.int16) & 0x7FFF
+    up = (mag + 1).view(torch.bfloat16).float() - mag.view(torch.bfloat16).float()
+    assert torch.all(res.float().abs() <= 0.5 * up)
+    empty = ~oracle.explicit_mask(w.cu_q, w.cu_k, w.mask_mode, w.window).any(axis=1)
+    if empty.any():
+        rows = torch.from_numpy(np.nonzero(empty)[0]).cuda()
+        assert torch.all(out[rows].view(torch.int16) == 0)
+        assert torch.all(res[rows].view(torch.int16) == 0)
 
 
 def test_dropout_replays_across_packings():
@@ -152,16 +196,20 @@ def test_dropout_zero_probability_is_attn_fwd():
     assert np.array_equal(to_np(out), to_np(out2)) and np.array_equal(to_np(lse), to_np(lse2))
 
 
-def test_dropout_train_full_size():
+@pytest.mark.parametrize("residual", [False, True], ids=["exact_d_pass", "residual"])
+def test_dropout_train_full_size(residual):
     """The training workload (B=2, Hq=32, Hkv=8, N=8192, d=128, top-left) with p = 0.1:
-    full GPU forward + backward; the oracle replays the realisation on one (sequence, K/V
-    head group): O and LSE of its 4 query heads, dQ, dK, dV of the group."""
+    full GPU forward + backward (D from the backward's own pass, or from the forward's
+    output residual as the bench runs it); the oracle replays the realisation on one
+    (sequence, K/V head group): O and LSE of its 4 query heads, dQ, dK, dV of the group."""
     w = wl.train_bf16()
     t = to_device(w)
     p, seed = 0.1, 2026
-    print("dropout train full size", flush=True)
-    out, lse = fwd_drop(w, t, p, seed)
-    dq, dk, dv = bwd_drop(w, t, out, lse, p, seed)
+    print(f"dropout train full size residual={residual}", flush=True)
+    res = residual_buffer(t) if residual else None
+    out, lse = fwd_drop(w, t, p, seed, res)
+    dq, dk, dv = bwd_drop(w, t, out, lse, p, seed, res)
+    del res
     o, l, gq, gk, gv = (to_np(x) for x in (out, lse, dq, dk, dv))
     for x in (o, l, gq, gk, gv):
         assert np.all(np.isfinite(x))
@@ -180,10 +228,12 @@ def test_dropout_train_full_size():
     assert_close(gv[rows][:, g], rv[rows][:, g], *BF16_TOL, "dropout train dV")
 
 
-def test_dropout_canaries_no_out_of_bounds_writes():
-    """The dropout forward and backward write only inside their outputs: O, LSE, dQ, dK, dV
-    land inside larger buffers whose slack holds sentinels, and every sentinel survives.
-    Keys no query can see get exactly zero dK/dV, whatever the realisation."""
+@pytest.mark.parametrize("residual", [False, True], ids=["exact_d_pass", "residual"])
+def test_dropout_canaries_no_out_of_bounds_writes(residual):
+    """The dropout forward and backward write only inside their outputs: O, LSE, the output
+    residual, dQ, dK, dV land inside larger buffers whose slack holds sentinels, and every
+    sentinel survives. Keys no query can see get exactly zero dK/dV, whatever the
+    realisation."""
     import torch
     import exact_attention_tiled_amd as eat
     lq, lk = [40, 3, 90], [10, 200, 90]
@@ -199,17 +249,18 @@ def test_dropout_canaries_no_out_of_bounds_writes():
 
     bo, out = padded(t["q"].shape, t["q"].dtype)
     bl, lse = padded((w.hq, w.total_q), torch.float32)
+    br, res = padded(t["q"].shape, t["q"].dtype) if residual else (None, None)
     eat.attn_fwd_dropout(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q,
                          w.max_seqlen_k, w.scale, w.mask_mode, w.window, 0.25, 777, out=out,
-                         lse=lse)
+                         lse=lse, out_residual=res)
     bq, dq = padded(t["q"].shape, t["q"].dtype)
     bk, dk = padded(t["k"].shape, t["k"].dtype)
     bv, dv = padded(t["v"].shape, t["v"].dtype)
     eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out, lse, t["dout"], t["cu_q"], t["cu_k"],
                          w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode, w.window, 0.25,
-                         777, dq=dq, dk=dk, dv=dv)
+                         777, dq=dq, dk=dk, dv=dv, out_residual=res)
     torch.cuda.synchronize()
-    for buf in (bo, bl, bq, bk, bv):
+    for buf in (bo, bl, bq, bk, bv) + ((br,) if residual else ()):
         assert torch.all(buf[:pad] == sentinel) and torch.all(buf[-pad:] == sentinel)
     m = oracle.explicit_mask(w.cu_q, w.cu_k, w.mask_mode, w.window)
     unseen = torch.from_numpy(np.nonzero(~m.any(axis=0))[0]).cuda()

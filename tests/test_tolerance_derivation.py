@@ -116,6 +116,29 @@ def test_dropout_gradient_bound_is_derived():
     assert max(canary) <= 2e-2
 
 
+def test_dropout_residual_d_keeps_the_derived_bound():
+    """D formed from the stored output plus its bf16 rounding residual (what the backward
+    uses when the forward hands over the residual) is within about 2^-16 of the output's
+    magnitude of the exact D, so the model's gradients with that D need the same atol as
+    with the exact D (to 1e-3) on every edge workload and stay within DROPOUT_GRAD_TOL; the
+    canary workload stays within the standard bound."""
+    for d, mode, window in DROPOUT_CASES:
+        w = dropout_backward_workload(d, mode, window)
+        ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, mode, window,
+                                   dropout_p=0.2, seed=99)
+        exact = model_backward(w, 0.2, 99)
+        res = model_backward(w, 0.2, 99, residual=True)
+        for g0, g1, r in zip(exact, res, ref):
+            a0, a1 = required_atol(g0, r), required_atol(g1, r)
+            assert abs(a1 - a0) <= 1e-3, (d, mode, window, a0, a1)
+            assert a1 * 1.1 <= DROPOUT_GRAD_TOL[0] + 1e-12
+    w = dropout_canary_workload()
+    ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
+                               w.window, dropout_p=0.25, seed=777)
+    got = model_backward(w, 0.25, 777, residual=True)
+    assert max(required_atol(g, r) for g, r in zip(got, ref)) <= 2e-2
+
+
 def test_model_within_standard_bound_on_standard_workloads():
     """On the backward edge workloads held to the standard bound on the GPU, the model needs
     no widening either: it does not overstate the operand roundings."""
