@@ -98,13 +98,16 @@ def test_splitk_race_exposure(poison_lib, dtype, nq, group, splits):
 
 # Backward workloads whose gradient bounds are derived on the CPU by the rounding model
 # (tests/test_tolerance_derivation.py): the seed-21 edges stay inside the standard bound,
-# the seed-42 dropout edges need DROPOUT_GRAD_TOL.
-BWD_CASES = [(64, 1, 0, 0.0), (128, 2, 0, 0.0), (128, 0, 0, 0.0), (64, 1, 70, 0.0),
-             (64, 1, 0, 0.2), (128, 2, 0, 0.2), (128, 1, 70, 0.2)]
+# the seed-42 dropout edges need DROPOUT_GRAD_TOL. The last flag runs the dropout forward
+# that also writes the output residual (its second PV contraction) and the backward that
+# forms D from it.
+BWD_CASES = [(64, 1, 0, 0.0, False), (128, 2, 0, 0.0, False), (128, 0, 0, 0.0, False),
+             (64, 1, 70, 0.0, False), (64, 1, 0, 0.2, False), (128, 2, 0, 0.2, False),
+             (128, 1, 70, 0.2, False), (64, 1, 0, 0.2, True), (128, 0, 0, 0.2, True)]
 
 
-@pytest.mark.parametrize("d,mode,window,dropout_p", BWD_CASES)
-def test_backward_race_exposure(poison_lib, d, mode, window, dropout_p):
+@pytest.mark.parametrize("d,mode,window,dropout_p,residual", BWD_CASES)
+def test_backward_race_exposure(poison_lib, d, mode, window, dropout_p, residual):
     import exact_attention_tiled_amd as eat
     if dropout_p == 0.0:
         w = wl.random_workload((21, d, mode), EDGE_Q, EDGE_K, 4, 2, d, "bf16", mode, window,
@@ -113,7 +116,8 @@ def test_backward_race_exposure(poison_lib, d, mode, window, dropout_p):
         edge = [0, 1, 63, 64, 65, 127, 128, 129]
         w = wl.random_workload((42, d, mode), edge + [5, 200], edge[::-1] + [300, 3], 4, 2, d,
                                "bf16", mode, window, with_dout=True, name="drop-bwd")
-    print(f"poisoned backward d={d} mode={mode} window={window} p={dropout_p}", flush=True)
+    print(f"poisoned backward d={d} mode={mode} window={window} p={dropout_p} "
+          f"residual={residual}", flush=True)
     t = to_device(w)
     args = (t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
             w.scale, w.mask_mode, w.window)
@@ -123,13 +127,17 @@ def test_backward_race_exposure(poison_lib, d, mode, window, dropout_p):
             out, lse = eat.attn_fwd(*args)
             g = eat.attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], *args[3:])
         else:
-            out, lse = eat.attn_fwd_dropout(*args, dropout_p, 99)
+            import torch
+            res = torch.empty_like(t["q"]) if residual else None
+            out, lse = eat.attn_fwd_dropout(*args, dropout_p, 99, out_residual=res)
             g = eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out, lse, t["dout"], *args[3:],
-                                     dropout_p, 99)
+                                     dropout_p, 99, out_residual=res)
+            if residual:
+                return (out, lse) + tuple(g) + (res,)
         return (out, lse) + tuple(g)
 
     rel, poi = _both(poison_lib, run)
-    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), rel, poi):
+    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV", "residual"), rel, poi):
         assert _bitwise(a, b), f"poisoned {name} differs from the release build"
     kw = {} if dropout_p == 0.0 else {"dropout_p": dropout_p, "seed": 99}
     ref = oracle.attention_bwd(w.q, w.k, w.v, w.dout, w.cu_q, w.cu_k, w.scale, w.mask_mode,
