@@ -635,11 +635,17 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
       prefill_steady<D, 1>(c, r, j, sb, sa, kbuf, vbuf);
       prefill_steady<D, 0>(c, r, j + 1, sa, sb, kbuf, vbuf);
     }
+    // Under a causal mask the last stage holds keys that the upper rows of the tile never
+    // see: a wave none of whose rows sees any of them leaves out that stage's weights and
+    // PV contraction (a uniform branch; they would add exact zeros).
+    const int klast = kstart + (nst - 1) * BN;
+    const bool skip_last =
+        nst > 1 && block_class(wp0, wp1, klast, klast + BN, g, p.mode, p.window) == 0;
     if (j < nst) {
       prefill_steady<D, 1>(c, r, j, sb, sa, kbuf, vbuf);
-      prefill_tail<D, 1>(c, r, sb, vbuf);
+      if (!skip_last) prefill_tail<D, 1>(c, r, sb, vbuf);
     } else {
-      prefill_tail<D, 0>(c, r, sa, vbuf);
+      if (!skip_last) prefill_tail<D, 0>(c, r, sa, vbuf);
     }
   }
 
