@@ -622,11 +622,22 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
       wait_vmem();
     }
     __syncthreads();
-    // Stage 0: scores only.
-    sa[0] = f32x16{};
-    sa[1] = f32x16{};
-    M::qk2(sa, kbuf0, qr, of);
-    r.mask_prev = block_class(wp0, wp1, kstart, kstart + BN, g, p.mode, p.window) != 2;
+    // Stage 0: scores only. Under a window its keys can lie before every row of a lower
+    // wave: that wave takes -inf scores instead of the contraction (its weights are then
+    // exact zeros, as the per-lane test would make them).
+    const int cls0 = block_class(wp0, wp1, kstart, kstart + BN, g, p.mode, p.window);
+    if (cls0 == 0) {
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2) {
+        sa[0][r2] = neg_inf();
+        sa[1][r2] = neg_inf();
+      }
+    } else {
+      sa[0] = f32x16{};
+      sa[1] = f32x16{};
+      M::qk2(sa, kbuf0, qr, of);
+    }
+    r.mask_prev = cls0 == 1;
     wait_vmem();
     vst.write(vbuf0);
     __syncthreads();
