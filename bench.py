@@ -15,7 +15,9 @@ forward, cached decode at Nq = 1, 4, 16 and the Nq = 64 > Nk = 32 edge (GB/s), a
 training forward + backward, causal, with a 1024-key window, and with dropout p = 0.1.
 
 Protocol ("Attention Kernel Portability and Benchmarking", fourth and fifth sections):
-outputs are validated against the fp64 oracle on a sample before timing; warm-up calls;
+outputs are validated against the fp64 oracle on a sample before timing; at least 0.25 s of
+untimed calls (the device's clocks rise from idle over about 0.1 s of work) and the W
+warm-up calls;
 the K timed steps are bracketed by device synchronisation and by two HIP events on the
 launch stream (their mean gives ms per launch for the roofline); a second pass of K steps
 with per-step events gives median / p10 / p90 / max. The oracle is timed on the host cores
@@ -115,13 +117,36 @@ def stored_traffic(kernel: str, workload: str):
 # timing
 # ----------------------------------------------------------------------------------------
 
+# Untimed steps before the warm-up steps: after the host-side validation the device has
+# been idle, and its clocks take about 0.1 s of sustained work to rise. Measured on the
+# dense forward (50 timed steps): 10 warm-up steps gave 677-706 TFLOP/s, 100 gave 768 and
+# 1000 (80 ms of work) 864; the timed region itself is unchanged (exactly K steps).
+SETTLE_SECONDS = 0.25
+
+
+def settle(fn, seconds: float = SETTLE_SECONDS) -> int:
+    """Run fn untimed until `seconds` of wall time have passed (synchronising every few
+    calls so the time is device time, not queueing); returns the number of calls."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return n
+
+
 def time_steps(fn, steps: int, warmup: int):
-    """Warm-up, then K timed steps between two HIP events on the launch stream (bracketed by
-    device synchronisation): returns wall seconds, the mean event time per step, and the
-    per-step event times of a second, separate pass of K steps (distribution only: the
-    per-step event pairs add their own gaps, so they are kept out of the timed region)."""
+    """Settle, W warm-up steps, then K timed steps between two HIP events on the launch
+    stream (bracketed by device synchronisation): returns wall seconds, the mean event time
+    per step, and the per-step event times of a second, separate pass of K steps
+    (distribution only: the per-step event pairs add their own gaps, so they are kept out of
+    the timed region)."""
     import torch
     stream = torch.cuda.current_stream()
+    settle(fn)
     for _ in range(warmup):
         fn()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -560,7 +585,9 @@ def main():
         "value": "work per step x K / wall time of the K back-to-back steps (synchronised)",
         "roofline.achieved": "work per launch / mean launch time from two HIP events around "
                              "the same K steps on the launch stream",
-        "value_median": "work per step / median of K separately bracketed steps"}
+        "value_median": "work per step / median of K separately bracketed steps",
+        "warmup": f"untimed steps for at least {SETTLE_SECONDS} s (device clocks rise from "
+                  "idle), then W warm-up steps, before each timed pass"}
     line["config"]["workload"] = w.name
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
