@@ -74,7 +74,7 @@ __device__ __forceinline__ void visible_queries(int k0, int k1, const SeqGeom& g
 // empty rows mapped to +inf (so every recomputed P of such a row is exactly 0). One wave
 // per (query token, query head).
 // ---------------------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool RES>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
                                                       const T* __restrict__ out_res,
                                                       const T* __restrict__ dout,
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
   const int sub = tid % LPR;
   const size_t base = (size_t)item * D + sub * 8;
   float acc = 0.0f;
-  if (out_res != nullptr) {
+  if constexpr (RES) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       acc += ((float)out[base + i] + (float)out_res[base + i]) * (float)dout[base + i];
@@ -910,10 +910,15 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   float* lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + vecb);
   const long items = (long)f.total_q * f.hq;
   if (items > 0) {
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((items + 256 / (D / 8) - 1) / (256 / (D / 8)))),
-                       dim3(256), 0, st,
-                       static_cast<const T*>(a.out), static_cast<const T*>(a.out_res),
-                       static_cast<const T*>(a.dout), a.lse, f.total_q, f.hq, dvec, lse2);
+    const dim3 grid((unsigned)((items + 256 / (D / 8) - 1) / (256 / (D / 8))));
+    if (a.out_res != nullptr)
+      hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), grid, dim3(256), 0, st,
+                         static_cast<const T*>(a.out), static_cast<const T*>(a.out_res),
+                         static_cast<const T*>(a.dout), a.lse, f.total_q, f.hq, dvec, lse2);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<T, D, false>), grid, dim3(256), 0, st,
+                         static_cast<const T*>(a.out), nullptr, static_cast<const T*>(a.dout),
+                         a.lse, f.total_q, f.hq, dvec, lse2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
