@@ -373,21 +373,19 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
     if constexpr (RES) {
       // The residual x - bf16(x) of every stored element (bf16, |r| <= half an ulp of the
       // output), so that the backward can form D = rowsum(dO * O) from the unrounded O.
-      {
-        __bf16* rrow = p.out_res + ((size_t)(g.q_start + pq) * p.hq + h) * D;
+      __bf16* rrow = p.out_res + ((size_t)(g.q_start + pq) * p.hq + h) * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            float x[4];
+        for (int a = 0; a < 4; ++a) {
+          float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float y = nonempty ? o[db][4 * a + e] * inv : 0.0f;
-              x[e] = y - (float)(__bf16)y;
-            }
-            M::store4(rrow + db * 32 + 8 * a + 4 * hg, x[0], x[1], x[2], x[3]);
+          for (int e = 0; e < 4; ++e) {
+            const float y = nonempty ? o[db][4 * a + e] * inv : 0.0f;
+            x[e] = y - (float)(__bf16)y;
           }
-      }
+          M::store4(rrow + db * 32 + 8 * a + 4 * hg, x[0], x[1], x[2], x[3]);
+        }
     }
     if (hg == 0)
       p.lse[(size_t)h * p.total_q + g.q_start + pq] =
