@@ -66,7 +66,7 @@ def test_pair_counts_of_the_named_workloads():
 
 
 def test_more_than_one_gpu_is_refused():
-    """This build measures one GPU: --gpus above 1 exits before touching a device."""
+    """The bench measures one GPU: --gpus above 1 exits before touching a device."""
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
