@@ -579,8 +579,6 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
   const int pq = wp0 + (lane & 31);
   const bool qvalid = pq < wp1;
   bf16x8 qr[M::QREGS];
-  const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)(g.q_start + pq) * p.hq + h) * D;
-  M::load_q(qr, qrow, qvalid, p.neg != 0, lane);
   const typename M::Offsets of = M::offsets(lane);
 
   int kstart, nst;
@@ -604,10 +602,19 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
   f32x16 sa[2], sb[2];  // scores of even / odd stages
 
   if (nst > 0) {
-    // K_0, V_0 and K_1 are all requested before the first wait: the tile's start costs one
-    // memory round trip, not three.
+    // The tile's Q arrives by DMA as two 64-row halves in the V^T buffers (free until stage
+    // 0's V^T is written): whole 256-byte rows per request instead of the 32-byte pieces of
+    // the operand layout. Then K_0, V_0 and K_1: everything is requested before the first
+    // wait, so the tile's start costs one memory round trip, not three.
+    {
+      const uint32_t qstride = (uint32_t)(p.hq * D * 2);
+      const char* qg = static_cast<const char*>(p.q) + ((size_t)(g.q_start + p0) * p.hq + h) * D * 2;
+      DmaStager<ROWB, 64, 4> qdma;
+      qdma.init(wave, lane, qstride);
+      qdma.issue(qg, p1 - p0, qstride, vbuf0);
+      qdma.issue(qg + (size_t)64 * qstride, p1 - p0 - 64, qstride, vbuf1);
+    }
     dma.issue(kg + (size_t)kstart * rstride, g.len_k - kstart, rstride, kbuf0);
-    vst.poison(vbuf0);
     vst.issue(vg + (size_t)kstart * rstride, g.len_k - kstart, rstride);
     if (nst > 1) {
       dma.issue(kg + (size_t)(kstart + BN) * rstride, g.len_k - kstart - BN, rstride, kbuf1);
@@ -620,6 +627,18 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
       wait_vmem();
     }
     __syncthreads();
+    {
+      // This wave's 32 Q rows as QK^T operands (rows past the tile end arrived as zeros);
+      // the operand layout is the K tile's, so the K offsets apply.
+      const char* qt = (wave < 2 ? vbuf0 : vbuf1) + (wave & 1) * 32 * ROWB;
+      const int flip = p.neg != 0 ? (int)0x80008000 : 0;  // negative scale: flip Q's sign
+#pragma unroll
+      for (int st = 0; st < M::QREGS; ++st) {
+        i32x4 x = *reinterpret_cast<const i32x4*>(qt + of.k[st]);
+        x ^= i32x4{flip, flip, flip, flip};
+        qr[st] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
     // Stage 0: scores only. Under a window its keys can lie before every row of a lower
     // wave: that wave takes -inf scores instead of the contraction (its weights are then
     // exact zeros, as the per-lane test would make them).
@@ -637,6 +656,8 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_bf16_kernel(FwdParams p) {
     }
     r.mask_prev = cls0 == 1;
     wait_vmem();
+    __syncthreads();  // every wave has its Q operands: vbuf0 takes V^T_0
+    vst.poison(vbuf0);
     vst.write(vbuf0);
     __syncthreads();
     int j = 1;
