@@ -114,3 +114,36 @@ def test_dropout_reads_only_inside_inputs(residual):
     for name, a, b in zip(("dQ", "dK", "dV"), g1, g2):
         assert bitwise(a, b), name
     assert all(bool(torch.isfinite(x.float()).all()) for x in (o2, *g2))
+
+
+def test_repeat_runs_are_bitwise_identical():
+    """No atomics and a fixed reduction order on every path: the split-K decode, the backward
+    and the dropout backward (with the output residual) give bitwise the same results when
+    run twice on the same inputs (the prefill's own check is in test_gpu_fwd.py)."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    w = wl.random_workload(64, EDGE_Q, EDGE_K, 8, 2, 128, "bf16", wl.MASK_CAUSAL_BOTTOM_RIGHT,
+                           0, with_dout=True, name="repeat")
+    t = to_device(w)
+    args = (w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode, w.window)
+    runs = []
+    for _ in range(2):
+        o, l = eat.attn_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], *args)
+        g = eat.attn_bwd(t["q"], t["k"], t["v"], o, l, t["dout"], t["cu_q"], t["cu_k"], *args)
+        r = torch.empty_like(t["q"])
+        od, ld = eat.attn_fwd_dropout(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], *args, 0.3,
+                                      5, out_residual=r)
+        gd = eat.attn_bwd_dropout(t["q"], t["k"], t["v"], od, ld, t["dout"], t["cu_q"],
+                                  t["cu_k"], *args, 0.3, 5, out_residual=r)
+        dec = wl.random_workload(65, [1, 4, 16, 3], [3000, 129, 1000, 2], 8, 2, 128, "bf16",
+                                 wl.MASK_CAUSAL_BOTTOM_RIGHT, name="repeat-decode")
+        td = to_device(dec)
+        os_, ls = eat.attn_fwd(td["q"], td["k"], td["v"], td["cu_q"], td["cu_k"],
+                               dec.max_seqlen_q, dec.max_seqlen_k, dec.scale, dec.mask_mode,
+                               path=eat.ATTN_PATH_SPLITK)
+        runs.append((o, l, *g, od, ld, r, *gd, os_, ls))
+    torch.cuda.synchronize()
+    names = ("O", "LSE", "dQ", "dK", "dV", "dropout O", "dropout LSE", "residual",
+             "dropout dQ", "dropout dK", "dropout dV", "split-K O", "split-K LSE")
+    for name, a, b in zip(names, *runs):
+        assert bitwise(a, b), name
