@@ -35,7 +35,11 @@ struct BwdParams {
   int mode, window;
   const float* lse2;   // [hq, total_q] LSE * log2(e); +inf for rows with no allowed key
   const float* dvec;   // [hq, total_q] rowsum(dO * O)
-  float* dvec_out;     // D written by the D pass (same buffer as dvec)
+  float* dvec_out;     // D written by the D pass or the dQ kernel (same buffer as dvec)
+  float* lse2_out;     // LSE * log2(e) written by the dQ kernel (same buffer as lse2)
+  const float* lse;    // the forward's LSE (natural log), read by the dQ kernel
+  const __bf16* out;      // the forward's output, and its rounding residual (or null)
+  const __bf16* out_res;
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -74,15 +78,13 @@ __device__ __forceinline__ void visible_queries(int k0, int k1, const SeqGeom& g
 // empty rows mapped to +inf (so every recomputed P of such a row is exactly 0). One wave
 // per (query token, query head).
 // ---------------------------------------------------------------------------------------
-template <typename T, int D, bool RES>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
-                                                      const T* __restrict__ out_res,
                                                       const T* __restrict__ dout,
                                                       const float* __restrict__ lse, int total_q,
                                                       int hq, float* __restrict__ dvec,
                                                       float* __restrict__ lse2) {
-  // D / 8 lanes per (token, head) row, 16 bytes of O and dO each. With out_res (bf16
-  // dropout), O is the stored output plus its rounding residual.
+  // D / 8 lanes per (token, head) row, 16 bytes of O and dO each.
   constexpr int LPR = D / 8;
   const int tid = threadIdx.x;
   const long item = (long)blockIdx.x * (256 / LPR) + tid / LPR;
@@ -90,14 +92,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
   const int sub = tid % LPR;
   const size_t base = (size_t)item * D + sub * 8;
   float acc = 0.0f;
-  if constexpr (RES) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      acc += ((float)out[base + i] + (float)out_res[base + i]) * (float)dout[base + i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc += (float)out[base + i] * (float)dout[base + i];
-  }
+  for (int i = 0; i < 8; ++i) acc += (float)out[base + i] * (float)dout[base + i];
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (sub == 0) {
@@ -375,7 +371,11 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
 // formed from the stored output. Both equal rowsum(dO * O) for the exact O; with dropout
 // even a one-key row stores a rounded 1.25 v, whose rounding no longer cancels in
 // dS = P (dP - D) and would move dK of such keys far beyond the gradient tolerance.
-template <int D, bool DROP = false, bool DONLY = false>
+// PRE > 0 (bf16; runs before the dK/dV kernel): each query row's D = rowsum(dO * O) (with
+// PRE == 2, O = the stored output plus its rounding residual) and LSE * log2(e) are formed
+// here from the forward's outputs and written for the dK/dV kernel, so the backward needs
+// no preprocess pass of its own.
+template <int D, bool DROP = false, bool DONLY = false, int PRE = 0>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   typedef Mma<__bf16, D> M;
   constexpr int BM = FWD_BM, BN = FWD_BN, ROWB = M::ROWB, TILE = BN * ROWB;
@@ -407,8 +407,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   M::load_q(qr, p.q + qoff, qvalid, false, lane);
   M::load_q(dor, p.dout + qoff, qvalid, false, lane);
   const size_t li = (size_t)h * p.total_q + g.q_start + pq;
-  const float l2 = qvalid ? p.lse2[li] : __builtin_inff();
-  const float dvl = (!DONLY && qvalid) ? p.dvec[li] : 0.0f;
+  float l2, dvl;
+  if constexpr (PRE > 0) {
+    bf16x8 orr[M::QREGS];
+    M::load_q(orr, p.out + qoff, qvalid, false, lane);
+    float part = 0.0f;
+    if constexpr (PRE == 2) {
+      bf16x8 rr[M::QREGS];
+      M::load_q(rr, p.out_res + qoff, qvalid, false, lane);
+#pragma unroll
+      for (int st = 0; st < M::QREGS; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          part += ((float)orr[st][e] + (float)rr[st][e]) * (float)dor[st][e];
+    } else {
+#pragma unroll
+      for (int st = 0; st < M::QREGS; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += (float)orr[st][e] * (float)dor[st][e];
+    }
+    const float dtot = sum_halves(part);  // lanes l and l ^ 32 hold the two row halves
+    const float lv = qvalid ? p.lse[li] : neg_inf();
+    l2 = lv == neg_inf() ? __builtin_inff() : lv * LOG2E;
+    dvl = qvalid ? dtot : 0.0f;
+    if (qvalid && lane < 32) {
+      p.dvec_out[li] = dtot;
+      p.lse2_out[li] = l2;
+    }
+  } else {
+    l2 = qvalid ? p.lse2[li] : __builtin_inff();
+    dvl = (!DONLY && qvalid) ? p.dvec[li] : 0.0f;
+  }
   float dsum = 0.0f;  // DONLY: this lane's part of sum_j P dP
   const typename M::Offsets of = M::offsets(lane);
 
@@ -909,16 +938,15 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   float* dvec = static_cast<float*>(ws);
   float* lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + vecb);
   const long items = (long)f.total_q * f.hq;
-  if (items > 0) {
-    const dim3 grid((unsigned)((items + 256 / (D / 8) - 1) / (256 / (D / 8))));
-    if (a.out_res != nullptr)
-      hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), grid, dim3(256), 0, st,
-                         static_cast<const T*>(a.out), static_cast<const T*>(a.out_res),
-                         static_cast<const T*>(a.dout), a.lse, f.total_q, f.hq, dvec, lse2);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<T, D, false>), grid, dim3(256), 0, st,
-                         static_cast<const T*>(a.out), nullptr, static_cast<const T*>(a.dout),
-                         a.lse, f.total_q, f.hq, dvec, lse2);
+  const bool drop = f.drop_thr > 0;
+  // bf16 without dropout, or with the forward's output residual: the dQ kernel runs first
+  // and forms D and LSE * log2(e) itself (no preprocess pass); the dK/dV kernel follows.
+  const bool fused = std::is_same<T, __bf16>::value && (!drop || a.out_res != nullptr);
+  if (items > 0 && !fused) {
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>),
+                       dim3((unsigned)((items + 256 / (D / 8) - 1) / (256 / (D / 8)))),
+                       dim3(256), 0, st, static_cast<const T*>(a.out),
+                       static_cast<const T*>(a.dout), a.lse, f.total_q, f.hq, dvec, lse2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -947,12 +975,15 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
   p.nlogical = p.nslots * f.hkv;
   p.nslots_q = f.total_q / FWD_BM + f.num_seqs;
   p.nlogical_q = p.nslots_q * f.hq;
-  const bool drop = f.drop_thr > 0;
   p.seed_lo = (uint32_t)f.seed;
   p.seed_hi = (uint32_t)(f.seed >> 32);
   p.drop_thr = f.drop_thr;
   p.drop_scale = f.drop_scale;
   p.dvec_out = dvec;
+  p.lse2_out = lse2;
+  p.lse = a.lse;
+  p.out = static_cast<const __bf16*>(a.out);
+  p.out_res = static_cast<const __bf16*>(a.out_res);
   if constexpr (std::is_same<T, float>::value) {
     // fp32: one wave per 32-key / 32-query chunk slot (D = rowsum(dO * O) from the fp32
     // output is exact enough here: no separate D pass).
@@ -973,9 +1004,28 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  // Dropout: D = sum_j P dP needs the unrounded output. With the forward's residual the
-  // preprocess above already formed it; otherwise a pass of its own computes it exactly.
-  if (drop && a.out_res == nullptr && f.total_q > 0) {
+  if (fused) {
+    if (f.total_q > 0) {
+      const int grid = ((p.nlogical_q + 7) / 8) * 8;
+      if (drop)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, 2>), dim3(grid), dim3(256), 0, st, p);
+      else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, 1>), dim3(grid), dim3(256), 0, st, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (f.total_k > 0) {
+      const int grid = ((p.nlogical + 7) / 8) * 8;
+      if (drop)
+        hipLaunchKernelGGL((bwd_main_kernel<D, true>), dim3(grid), dim3(512), 0, st, p);
+      else
+        hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(grid), dim3(512), 0, st, p);
+    }
+    return hipGetLastError();
+  }
+  // Dropout without the residual: D = sum_j P dP needs the unrounded output, so a pass of
+  // its own computes it exactly before the dK/dV and dQ kernels.
+  if (drop && f.total_q > 0) {
     const int grid = ((p.nlogical_q + 7) / 8) * 8;
     hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3(grid), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
