@@ -1,4 +1,6 @@
-// attn_bwd.hip - backward kernels: preprocess, main (dK, dV and dQ contributions), dQ convert.
+// attn_bwd.hip - backward kernels: dQ (query-major; for bf16 it also forms D and the LSE in
+// base 2 and runs first), dK/dV (key-major), the preprocess used by fp32 and by dropout
+// without the forward's output residual, and the fp32 kernels.
 //
 // The backward rebuilds P from the saved log-sum-exp instead of storing it, deciding which
 // pairs count with the forward's own interval rules, so that its mask is the forward's
@@ -9,7 +11,7 @@
 //   dV += P^T dO          dP = dO V^T          dS = P (dP - D),  D = rowsum(dO * O)
 //   dK += scale dS^T Q    dQ += scale dS K
 //
-// Main kernel: one workgroup = 8 waves = 128 keys of one (sequence, K/V head), looping
+// dK/dV kernel: one workgroup = 8 waves = 128 keys of one (sequence, K/V head), looping
 // over every query head of the group and every 64-query tile that can see those keys (see
 // bwd_main_kernel for the split of work between waves).
 #include <type_traits>
