@@ -41,15 +41,6 @@ int validate_common(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t 
   return ATTN_OK;
 }
 
-// The backward kernels take bf16 tensors only: an fp32 call is rejected here, before any
-// launch, like every other unsupported argument.
-int validate_bwd(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
-                 int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype, int32_t mode,
-                 int32_t window) {
-  return validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
-                         window);
-}
-
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_device_cu[64];  // compute units per device (0 unknown)
 
@@ -321,8 +312,8 @@ int attn_fwd_no_workspace(const void* q, const void* k, const void* v, const int
 size_t attn_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_q,
                                int32_t max_k, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
                                int32_t mode, int32_t window) {
-  if (validate_bwd(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
-                   window) != ATTN_OK)
+  if (validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                      window) != ATTN_OK)
     return 0;
   return attn::bwd_workspace_bytes(total_q, hq, d);
 }
@@ -332,8 +323,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              int32_t total_q, int32_t total_k, int32_t max_q, int32_t max_k, int32_t hq,
              int32_t hkv, int32_t d, int32_t dtype, float scale, int32_t mode, int32_t window,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = validate_bwd(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
-                        window);
+  int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                           window);
   if (rc != ATTN_OK) return rc;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   const size_t need = attn::bwd_workspace_bytes(total_q, hq, d);
@@ -465,8 +456,8 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* ou
                      float scale, int32_t mode, int32_t window, float dropout_p, uint64_t seed,
                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  int rc = validate_bwd(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
-                        window);
+  int rc = validate_common(num_seqs, total_q, total_k, max_q, max_k, hq, hkv, d, dtype, mode,
+                           window);
   if (rc != ATTN_OK) return rc;
   if (out_residual != nullptr && dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
