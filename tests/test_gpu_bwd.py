@@ -137,6 +137,45 @@ def test_train_full_size(window):
         assert_close(gv[krows][:, g], rv, *BF16_TOL, f"train dV s{s} g{g}")
 
 
+def test_ragged_gqa_bwd_full_size():
+    """The packed ragged GQA workload's packing (16384 tokens, lengths U[1,4096] plus 63, 64,
+    65, 127, 128, 129; Hq=32, Hkv=8, d=128, causal) with a loss gradient: GPU forward and
+    backward, then every sequence on one K/V group (the groups rotate over the sequences) and
+    all 8 groups of the longest sequence against the oracle at the standard bound: the
+    gradients of a packed sequence must not take anything from its neighbours ("Causal Mask
+    and Ragged Sequence Layouts", sixth section). Values are standard normal here. With the
+    forward test's per-sequence value offsets (values up to ~200) the bf16 rounding of the
+    stored output, from which D = rowsum(dO * O) is formed, no longer cancels in
+    dS = P (dP - D): the CPU rounding model then needs atol ~2 for dQ and dK."""
+    import torch
+    import oracle_pool as op
+    w = wl.ragged_gqa(with_dout=True, v_offsets=False)
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    dq, dk, dv = run_bwd(w, t, out, lse)
+    gq, gk, gv = to_np(dq), to_np(dk), to_np(dv)
+    del t, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    for x in (gq, gk, gv):
+        assert np.all(np.isfinite(x))
+    lens = np.diff(w.cu_q)
+    longest = int(np.argmax(lens))
+    slices = [(s, s % w.hkv) for s in range(w.num_seqs)]
+    slices += [(longest, g) for g in range(w.hkv) if g != longest % w.hkv]
+    print(f"ragged bwd full size: {w.num_seqs} sequences, {len(slices)} oracle tasks",
+          flush=True)
+    res = op.run("ragged_gqa", {"with_dout": True, "v_offsets": False},
+                 [(op.bwd_slice, (s, g)) for s, g in slices])
+    grp = w.hq // w.hkv
+    for (s, g), (rq, rk, rv) in zip(slices, res):
+        heads = list(range(g * grp, (g + 1) * grp))
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+        krows = slice(int(w.cu_k[s]), int(w.cu_k[s + 1]))
+        assert_close(gq[rows][:, heads], rq, *BF16_TOL, f"ragged dQ s{s} g{g}")
+        assert_close(gk[krows][:, g], rk, *BF16_TOL, f"ragged dK s{s} g{g}")
+        assert_close(gv[krows][:, g], rv, *BF16_TOL, f"ragged dV s{s} g{g}")
+
+
 # ----------------------------------------------------------------------------------------
 # fp32 backward (exact products, fp32 accumulation): the fp32 bound 1e-5 + 1e-5 |ref|
 # ----------------------------------------------------------------------------------------

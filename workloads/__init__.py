@@ -186,11 +186,16 @@ def dense_bf16(batch: int = 4, seqlen: int = 2048, heads: int = 16, d: int = 128
                            name=f"dense_bf16_b{batch}_h{heads}_n{seqlen}_d{d}")
 
 
-def ragged_gqa(seed: int = 3, total: int = 16384) -> Workload:
-    """Packed ragged GQA: 16384 tokens, lengths U[1,4096] + forced, Hq=32, Hkv=8, d=128."""
+def ragged_gqa(seed: int = 3, total: int = 16384, with_dout: bool = False,
+               v_offsets: bool = True) -> Workload:
+    """Packed ragged GQA: 16384 tokens, lengths U[1,4096] + forced, Hq=32, Hkv=8, d=128.
+
+    ``with_dout`` adds the loss gradient (drawn after q, k, v, which stay the same);
+    ``v_offsets=False`` keeps the values standard normal (the backward's variant)."""
     lens = ragged_lengths(seed, total=total)
     return random_workload((seed, 1), lens, lens, 32, 8, 128, "bf16", MASK_CAUSAL_TOP_LEFT,
-                           v_offsets=True, name=f"ragged_gqa_t{total}_hq32_hkv8_d128")
+                           v_offsets=v_offsets, with_dout=with_dout,
+                           name=f"ragged_gqa_t{total}_hq32_hkv8_d128")
 
 
 def decode(nq: int, nk: int = 32768, batch: int = 16) -> Workload:
