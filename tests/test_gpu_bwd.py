@@ -137,6 +137,36 @@ def test_train_full_size(window):
         assert_close(gv[krows][:, g], rv, *BF16_TOL, f"train dV s{s} g{g}")
 
 
+@pytest.mark.parametrize("window", [0, 300])
+def test_head_dim_64_full_size(window):
+    """head_dim 64 across many tiles: B=2, N=2048, Hq=16 over Hkv=4, causal top-left (and a
+    window of 300), the pipelined bf16 forward and the backward: O and LSE of every query
+    head and dQ, dK, dV of every K/V group of both sequences against the oracle at the
+    standard bounds."""
+    import oracle_pool as op
+    kw = {"window": window, "seqlen": 2048, "hq": 16, "hkv": 4, "d": 64}
+    w = wl.train_bf16(**kw)
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    dq, dk, dv = run_bwd(w, t, out, lse)
+    o, l = to_np(out), to_np(lse)
+    gq, gk, gv = to_np(dq), to_np(dk), to_np(dv)
+    del t, out, lse, dq, dk, dv
+    slices = [(s, g) for s in (0, 1) for g in range(4)]
+    tasks = [(op.fwd_slice, (s, list(range(4 * g, 4 * g + 4)))) for s, g in slices]
+    tasks += [(op.bwd_slice, (s, g)) for s, g in slices]
+    res = op.run("train_bf16", kw, tasks)
+    for (s, g), (ro, rl), (rq, rk, rv) in zip(slices, res[:len(slices)], res[len(slices):]):
+        heads = list(range(4 * g, 4 * g + 4))
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+        krows = slice(int(w.cu_k[s]), int(w.cu_k[s + 1]))
+        assert_close(o[rows][:, heads], ro, *BF16_TOL, f"d64 O s{s} g{g}")
+        assert_close(l[heads][:, rows], rl, 1e-3, 0.0, f"d64 LSE s{s} g{g}")
+        assert_close(gq[rows][:, heads], rq, *BF16_TOL, f"d64 dQ s{s} g{g}")
+        assert_close(gk[krows][:, g], rk, *BF16_TOL, f"d64 dK s{s} g{g}")
+        assert_close(gv[krows][:, g], rv, *BF16_TOL, f"d64 dV s{s} g{g}")
+
+
 def test_ragged_gqa_bwd_full_size():
     """The packed ragged GQA workload's packing (16384 tokens, lengths U[1,4096] plus 63, 64,
     65, 127, 128, 129; Hq=32, Hkv=8, d=128, causal) with a loss gradient: GPU forward and

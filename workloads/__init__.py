@@ -205,10 +205,11 @@ def decode(nq: int, nk: int = 32768, batch: int = 16) -> Workload:
                            name=f"decode_bf16_b{batch}_hq32_hkv8_nq{nq}_nk{nk}_d128")
 
 
-def train_bf16(window: int = 0, seqlen: int = 8192, batch: int = 2) -> Workload:
+def train_bf16(window: int = 0, seqlen: int = 8192, batch: int = 2, hq: int = 32, hkv: int = 8,
+               d: int = 128) -> Workload:
     """Forward+backward: B=2, Hq=32, Hkv=8, N=8192, d=128, bf16, causal TL (+ window)."""
     lens = [seqlen] * batch
     tag = f"_w{window}" if window > 0 else ""
-    return random_workload(5, lens, lens, 32, 8, 128, "bf16", MASK_CAUSAL_TOP_LEFT,
+    return random_workload(5, lens, lens, hq, hkv, d, "bf16", MASK_CAUSAL_TOP_LEFT,
                            window=window, with_dout=True,
-                           name=f"train_bf16_b{batch}_hq32_hkv8_n{seqlen}_d128{tag}")
+                           name=f"train_bf16_b{batch}_hq{hq}_hkv{hkv}_n{seqlen}_d{d}{tag}")
