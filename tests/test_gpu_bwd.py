@@ -167,6 +167,56 @@ def test_head_dim_64_full_size(window):
         assert_close(gv[krows][:, g], rv, *BF16_TOL, f"d64 dV s{s} g{g}")
 
 
+UNEQUAL_CASES = [  # (dtype, lq, lk, mode, d)
+    ("bf16", 1024, 4096, wl.MASK_CAUSAL_BOTTOM_RIGHT, 128),
+    ("bf16", 4096, 1024, wl.MASK_CAUSAL_BOTTOM_RIGHT, 128),
+    ("bf16", 3000, 2000, wl.MASK_CAUSAL_TOP_LEFT, 128),
+    ("f32", 1024, 1024, wl.MASK_CAUSAL_TOP_LEFT, 128),
+    ("f32", 700, 2100, wl.MASK_CAUSAL_BOTTOM_RIGHT, 64),
+]
+
+
+@pytest.mark.parametrize("case", range(len(UNEQUAL_CASES)))
+def test_unequal_lengths_full_size(case):
+    """Query and key lengths that differ, across many tiles (two sequences, Hq=8 over
+    Hkv=2): bottom-right with fewer queries than keys (a prefill against a cache) and with
+    more (the first Nq - Nk rows of each sequence see no key: exact zeros), top-left with
+    more queries than keys, and fp32 at its 1e-5 bound. Forward and backward of every head
+    against the oracle ("Causal Mask and Ragged Sequence Layouts", third and fourth
+    sections: explicit alignment, empty rows)."""
+    import oracle_pool as op
+    from gpu_util import F32_TOL
+    dtype, lq, lk, mode, d = UNEQUAL_CASES[case]
+    kw = dict(seed=(61, case), lengths_q=[lq, lq // 2], lengths_k=[lk, lk // 2], hq=8, hkv=2,
+              d=d, dtype=dtype, mask_mode=mode, with_dout=True, name="unequal")
+    w = wl.random_workload(**kw)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    t = to_device(w)
+    out, lse = run_fwd(w, t)
+    dq, dk, dv = run_bwd(w, t, out, lse)
+    o, l = to_np(out), to_np(lse)
+    gq, gk, gv = to_np(dq), to_np(dk), to_np(dv)
+    del t, out, lse, dq, dk, dv
+    slices = [(s, g) for s in (0, 1) for g in range(2)]
+    tasks = [(op.fwd_slice, (s, list(range(4 * g, 4 * g + 4)))) for s, g in slices]
+    tasks += [(op.bwd_slice, (s, g)) for s, g in slices]
+    res = op.run("random_workload", kw, tasks)
+    for (s, g), (ro, rl), (rq, rk, rv) in zip(slices, res[:len(slices)], res[len(slices):]):
+        heads = list(range(4 * g, 4 * g + 4))
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+        krows = slice(int(w.cu_k[s]), int(w.cu_k[s + 1]))
+        tag = f"{dtype} {lq}x{lk} mode {mode} s{s} g{g}"
+        assert_close(o[rows][:, heads], ro, *tol, f"O {tag}")
+        empty = ~np.isfinite(rl)
+        assert np.array_equal(~np.isfinite(l[heads][:, rows]), empty), f"empty rows {tag}"
+        assert np.all(o[rows][:, heads][empty.T] == 0), f"empty-row O {tag}"
+        assert_close(np.where(empty, 0.0, l[heads][:, rows]), np.where(empty, 0.0, rl), 1e-3,
+                     0.0, f"LSE {tag}")
+        assert_close(gq[rows][:, heads], rq, *tol, f"dQ {tag}")
+        assert_close(gk[krows][:, g], rk, *tol, f"dK {tag}")
+        assert_close(gv[krows][:, g], rv, *tol, f"dV {tag}")
+
+
 def test_ragged_gqa_bwd_full_size():
     """The packed ragged GQA workload's packing (16384 tokens, lengths U[1,4096] plus 63, 64,
     65, 127, 128, 129; Hq=32, Hkv=8, d=128, causal) with a loss gradient: GPU forward and
