@@ -173,6 +173,8 @@ UNEQUAL_CASES = [  # (dtype, lq, lk, mode, d)
     ("bf16", 3000, 2000, wl.MASK_CAUSAL_TOP_LEFT, 128),
     ("f32", 1024, 1024, wl.MASK_CAUSAL_TOP_LEFT, 128),
     ("f32", 700, 2100, wl.MASK_CAUSAL_BOTTOM_RIGHT, 64),
+    ("bf16", 16, 8192, wl.MASK_CAUSAL_BOTTOM_RIGHT, 128),   # split-K forward
+    ("f32", 4, 16384, wl.MASK_CAUSAL_BOTTOM_RIGHT, 64),     # split-K forward, fp32
 ]
 
 
@@ -181,7 +183,8 @@ def test_unequal_lengths_full_size(case):
     """Query and key lengths that differ, across many tiles (two sequences, Hq=8 over
     Hkv=2): bottom-right with fewer queries than keys (a prefill against a cache) and with
     more (the first Nq - Nk rows of each sequence see no key: exact zeros), top-left with
-    more queries than keys, and fp32 at its 1e-5 bound. Forward and backward of every head
+    more queries than keys, decode shapes (the forward takes the split-K path), and fp32 at
+    its 1e-5 bound. Forward and backward of every head
     against the oracle ("Causal Mask and Ragged Sequence Layouts", third and fourth
     sections: explicit alignment, empty rows)."""
     import oracle_pool as op
@@ -193,6 +196,11 @@ def test_unequal_lengths_full_size(case):
     tol = BF16_TOL if dtype == "bf16" else F32_TOL
     t = to_device(w)
     out, lse = run_fwd(w, t)
+    if lq <= 16:
+        import exact_attention_tiled_amd as eat
+        plan = eat.attn_describe_plan(t["q"], t["k"], t["cu_q"], w.max_seqlen_q, w.max_seqlen_k,
+                                      w.mask_mode)
+        assert "path=splitk" in plan, plan
     dq, dk, dv = run_bwd(w, t, out, lse)
     o, l = to_np(out), to_np(lse)
     gq, gk, gv = to_np(dq), to_np(dk), to_np(dv)
