@@ -267,7 +267,9 @@ def attn_fwd_dropout(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seql
                      out_residual=None):
     """Forward with dropout on the attention weights (attn_fwd_dropout in include/attn.h):
     returns (out, lse); lse is that of the undropped softmax. A bf16 `out_residual` tensor
-    shaped like q receives each output's rounding residual, for attn_bwd_dropout."""
+    shaped like q receives each output's rounding residual, for attn_bwd_dropout (also at
+    dropout_p = 0: the forward and backward of attn_fwd / attn_bwd with D formed from the
+    unrounded output)."""
     _dev(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, workspace, out_residual)
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
@@ -296,7 +298,8 @@ def attn_bwd_dropout(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_se
                      max_seqlen_k, scale, mask_mode, window, dropout_p, seed, *, dq=None,
                      dk=None, dv=None, workspace=None, out_residual=None):
     """Backward of attn_fwd_dropout with the same dropout_p and seed; returns (dq, dk, dv).
-    With the forward's `out_residual` the separate pass that computes D is skipped."""
+    With the forward's `out_residual` D comes from the unrounded output (and with dropout
+    the separate pass that computes D is skipped)."""
     _dev(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace,
          out_residual)
     dq = torch.empty_like(q) if dq is None else dq

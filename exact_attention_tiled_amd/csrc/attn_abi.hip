@@ -480,7 +480,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* ou
   a.f.drop_scale = dscale;
   a.f.seed = seed;
   a.out = out;
-  a.out_res = thr > 0 ? out_residual : nullptr;
+  a.out_res = out_residual;
   a.lse = lse;
   a.dout = dout;
   a.dq = dq;

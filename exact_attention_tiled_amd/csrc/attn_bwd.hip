@@ -1011,6 +1011,8 @@ static hipError_t bwd_typed(const BwdArgs& a, void* ws, hipStream_t st) {
       const int grid = ((p.nlogical_q + 7) / 8) * 8;
       if (drop)
         hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, 2>), dim3(grid), dim3(256), 0, st, p);
+      else if (a.out_res != nullptr)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, 2>), dim3(grid), dim3(256), 0, st, p);
       else
         hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, 1>), dim3(grid), dim3(256), 0, st, p);
       hipError_t e = hipGetLastError();

@@ -42,7 +42,7 @@ struct FwdParams {
   // dropout (prefill kernel instantiated with DROP only)
   uint32_t seed_lo, seed_hi, drop_thr;
   float drop_scale;
-  __bf16* out_res;  // bf16 with DROP: rounding residual of O (null = not wanted)
+  __bf16* out_res;  // bf16 (RES kernels only): rounding residual of O
 };
 
 // The exponent offset of a row moves only when a tile's maximum exceeds it by more than
@@ -59,8 +59,9 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 // (the other half of the row lives in lane l ^ 32).
 // With DROP the denominator still sums every weight, and the PV operand carries
 // weight * keep / (1 - p) (the keep flags of DropoutSite for this lane's query). With RES
-// (bf16) that operand z is also split: pk gets bf16(z) and pkr bf16(z - bf16(z)), so that
-// accumulating both against V gives the unrounded output to about 2^-16.
+// (bf16, with or without DROP) that operand z is also split: pk gets bf16(z) and pkr
+// bf16(z - bf16(z)), so that accumulating both against V gives the unrounded output to
+// about 2^-16.
 template <typename M, int NK, int D, bool DROP = false, bool RES = false>
 __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack (&pk)[NK],
                                              bool need_mask, int pq, int kpos0, const SeqGeom& g,
@@ -128,7 +129,15 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NK], typename M::PPack 
     }
   } else {
 #pragma unroll
-    for (int kb = 0; kb < NK; ++kb) l_run += M::pack_p(s[kb], pk[kb]);
+    for (int kb = 0; kb < NK; ++kb) {
+      if constexpr (RES) {
+        f32x16 lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lo[r] = s[kb][r] - (float)(__bf16)s[kb][r];
+        (void)M::pack_p(lo, pkr[kb]);
+      }
+      l_run += M::pack_p(s[kb], pk[kb]);
+    }
   }
 }
 
@@ -182,7 +191,7 @@ __device__ __forceinline__ bool prefill_tile(const FwdParams& p, int& h, int& s,
 }
 
 // Running state of one prefill wave (32 query rows) and its step over one 64-key stage.
-// RES (bf16 with DROP): the weights also go through V as their bf16 residuals.
+// RES (bf16): the weights also go through V as their bf16 residuals.
 template <typename T, int D, bool DROP = false, bool RES = false>
 struct PrefillWave {
   typedef Mma<T, D> M;
@@ -273,10 +282,11 @@ struct PrefillVStage<__bf16, D> {
 // load of stage j+1 is in flight while stage j is computed.
 // ---------------------------------------------------------------------------------------
 // With DROP the weights reaching V carry the dropout realisation (DropoutSite); this
-// kernel is the forward of every dropout call.
+// kernel is the forward of every dropout call. With RES (bf16) it also writes the output's
+// rounding residual, with or without dropout.
 template <typename T, int D, bool DROP = false, bool RES = false>
 __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdParams p) {
-  static_assert(!RES || (DROP && std::is_same<T, __bf16>::value), "residual: bf16 dropout");
+  static_assert(!RES || std::is_same<T, __bf16>::value, "residual: bf16 only");
   typedef Mma<T, D> M;
   constexpr int BM = FWD_BM, BN = FWD_BN, ROWB = M::ROWB;
   constexpr int KTILE = BN * ROWB, VTILE = PrefillVStage<T, D>::TILE_BYTES;
@@ -1258,6 +1268,14 @@ static hipError_t prefill_typed(const FwdArgs& a, void* ws, hipStream_t st) {
     }
     hipLaunchKernelGGL((fwd_prefill_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
   } else if constexpr (std::is_same<T, __bf16>::value) {
+    if (a.out_res != nullptr) {
+      // No dropout, but the caller wants the output's rounding residual (an exact D for the
+      // backward): the unpipelined kernel with the split PV operand.
+      p.out_res = static_cast<__bf16*>(a.out_res);
+      hipLaunchKernelGGL((fwd_prefill_kernel<T, D, false, true>), dim3(grid), dim3(256), 0, st,
+                         p);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((fwd_prefill_bf16_kernel<D>), dim3(grid), dim3(256), 0, st, p);
   } else {
     hipLaunchKernelGGL((fwd_prefill_kernel<T, D>), dim3(grid), dim3(256), 0, st, p);

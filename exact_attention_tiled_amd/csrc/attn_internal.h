@@ -24,14 +24,15 @@ struct FwdArgs {
   uint32_t drop_thr = 0;
   float drop_scale = 1.0f;
   uint64_t seed = 0;
-  // bf16 dropout forward only (may be null): O - round_bf16(O) per output element, in bf16
+  // bf16 forward through attn_fwd_dropout only (may be null): O - round_bf16(O) per output
+  // element, in bf16
   void* out_res = nullptr;
 };
 
 struct BwdArgs {
   FwdArgs f;          // q, k, v, cu, sizes, scale, mask (out/lse: forward outputs)
   const void* out;
-  const void* out_res = nullptr;  // bf16 dropout backward only: the forward's residual
+  const void* out_res = nullptr;  // bf16 (attn_bwd_dropout only): the forward's residual
   const float* lse;
   const void* dout;
   void* dq;

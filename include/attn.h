@@ -200,20 +200,26 @@ size_t attn_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_
  * position j: byte j % 4 of output word i % 4 of Philox4x32-10 (Salmon et al., SC'11) at
  * counter (i / 4, j / 4, h, s) and key (seed & 0xffffffff, seed >> 32), kept iff that byte
  * is >= t8 = floor(256 * dropout_p + 0.5) (computed in double from the float argument).
- *   dropout_p   in [0, 255.5/256), else ATTN_ERR_BAD_DROPOUT; t8 = 0 runs attn_fwd /
- *               attn_bwd unchanged
+ *   dropout_p   in [0, 255.5/256), else ATTN_ERR_BAD_DROPOUT; t8 = 0 without
+ *               out_residual runs attn_fwd / attn_bwd unchanged
  *   seed        any 64-bit value; attn_bwd_dropout must get the forward's dropout_p and seed
  * The forward always runs the prefill path (bf16 or fp32) and needs the workspace of
  * attn_fwd_dropout_workspace_size; the backward (bf16 or fp32, like attn_bwd) needs
  * attn_bwd_workspace_size. Other arguments, ownership and errors as attn_fwd / attn_bwd.
- *   out_residual  optional (may be NULL), bf16 only (ATTN_ERR_BAD_DTYPE otherwise), used
- *               only when t8 > 0: [total_q, Hq, head_dim] bf16 like out. The forward writes
- *               x - bf16(x) for every output element x it rounds into out; given the same
- *               buffer, the backward forms D = rowsum(dO * O) from out + out_residual.
- *               Without it the bf16 backward computes D = sum_u P dP in a pass of its own
- *               (the stored output's rounding no longer cancels in dS once weights are
- *               dropped and rescaled), which costs a recomputation of S and dP; the residual
- *               trades that pass for one more output-sized tensor kept from the forward.
+ *   out_residual  optional (may be NULL), bf16 only (ATTN_ERR_BAD_DTYPE otherwise):
+ *               [total_q, Hq, head_dim] bf16 like out. The forward writes x - bf16(x) for
+ *               every output element x it rounds into out; given the same buffer, the
+ *               backward forms D = rowsum(dO * O) from out + out_residual. Without it the
+ *               bf16 backward with t8 > 0 computes D = sum_u P dP in a pass of its own (the
+ *               stored output's rounding no longer cancels in dS once weights are dropped
+ *               and rescaled), which costs a recomputation of S and dP; the residual trades
+ *               that pass for one more output-sized tensor kept from the forward.
+ *               With t8 = 0 and out_residual given, the pair is attn_fwd / attn_bwd (prefill
+ *               path) with D formed from the unrounded output: the route for inputs where
+ *               the stored output's rounding does not cancel in dS either (|scale| far above
+ *               1/sqrt(head_dim), values with a large common offset), at the cost of an
+ *               unpipelined forward with a second PV contraction. The backward must get the
+ *               buffer its forward wrote: a residual never written gives wrong gradients.
  */
 int attn_fwd_dropout(const void* q, const void* k, const void* v,
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

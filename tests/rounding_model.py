@@ -4,9 +4,12 @@ Test infrastructure for deriving gradient tolerances: it is neither the oracle n
 path. Every value is first computed exactly (float64), then rounded to bf16 (round to
 nearest even) at exactly the points where the kernels hold bf16 data:
   forward  O = (sum_j bf16(p_j) v_j) / sum_j p_j, stored as bf16 (the PV contraction takes
-           the unnormalised weights as bf16 operands, the denominator sums them unrounded);
-  backward P rebuilt from the LSE, D = rowsum(dO * O_stored) (without dropout) or the exact
-           D = sum_j P dP (the dropout path's own D pass), dS = P (dP - D) and the dV operand
+           the unnormalised weights as bf16 operands, the denominator sums them unrounded;
+           each p_j is taken at the running exponent offset the kernel holds for its stage,
+           which the later rescales of the accumulator undo exactly);
+  backward P rebuilt from the LSE, D = rowsum(dO * O_stored) (without dropout), the exact
+           D = sum_j P dP (the dropout path's own D pass) or D from the stored output plus
+           its rounding residual, dS = P (dP - D) and the dV operand
            (P, or Z = P * keep / (1 - p) with dropout) rounded to bf16 before the
            contractions; dQ, dK, dV accumulated exactly and stored as bf16.
 The fp32 accumulations of the kernels (products of bf16 values are exact in fp32; sums carry
@@ -36,12 +39,35 @@ def required_atol(got, ref):
     return float(max(0.0, (err - RTOL * np.abs(ref)).max())) if err.size else 0.0
 
 
-def model_backward(w, dropout_p=0.0, seed=0, residual=False):
+def stage_offsets_of(logits2, stage=64, threshold=8.0):
+    """Per pair, the running exponent offset (log2 units) the prefill kernels hold when they
+    round that pair's weight 2^(logit - offset) to bf16. logits2: [rows, keys] scaled logits
+    in log2 units (-inf where excluded). Keys are visited in stages of `stage` from key 0; a
+    row's offset starts at -inf and becomes a stage's maximum when that exceeds the offset by
+    more than `threshold`. Excluded pairs get their row's maximum (0 for empty rows)."""
+    nq, nk = logits2.shape
+    rowmax = logits2.max(axis=1, initial=-np.inf)
+    rowmax = np.where(np.isfinite(rowmax), rowmax, 0.0)
+    off = np.repeat(rowmax[:, None], nk, axis=1)
+    m = np.full(nq, -np.inf)
+    for k0 in range(0, nk, stage):
+        blk = logits2[:, k0:k0 + stage]
+        mt = blk.max(axis=1)
+        m = np.where(mt > m + threshold, mt, m)
+        off[:, k0:k0 + stage] = np.where(np.isfinite(blk), m[:, None], off[:, k0:k0 + stage])
+    return off
+
+
+def model_backward(w, dropout_p=0.0, seed=0, residual=False, stage_offsets=True):
     """(dQ, dK, dV) of the rounding model for workload w (bf16 inputs, any mask, GQA). With
-    dropout, D is exact, or with residual=True formed from the stored output plus its bf16
+    residual=True (with or without dropout) D is formed from the stored output plus its bf16
     rounding residual; the forward that writes the residual splits each weight Z into
     bf16(Z) + bf16(Z - bf16(Z)) and accumulates both against V, so its unrounded output is
-    the exact one to about 2^-16."""
+    the exact one to about 2^-16. Otherwise D is exact with dropout and formed from the
+    stored output without. The forward's weights are rounded relative to the row maximum,
+    or with stage_offsets at the running offset the prefill kernels use (stage_offsets_of):
+    where one weight dominates a row (large |scale|) its rounding is exact at the row
+    maximum but not at another offset, and the stored output's rounding grows."""
     q, k, v, do = (np.asarray(a, np.float64) for a in (w.q, w.k, w.v, w.dout))
     thr = oracle.dropout_threshold(dropout_p)
     zscale = float(np.float32(256.0 / (256 - thr))) if thr > 0 else 1.0
@@ -64,6 +90,15 @@ def model_backward(w, dropout_p=0.0, seed=0, residual=False):
             logits = np.where(a, w.scale * q[qa:qb, h] @ k[ka:kb, g].T, -np.inf)
             m = np.where(rows, logits.max(axis=1, initial=-np.inf), 0.0)[:, None]
             pt = np.where(a, np.exp(logits - m), 0.0)
+            if stage_offsets:
+                # the kernel's weight at its running offset, and the exact rescale of that
+                # offset to the row maximum (the accumulator's later alpha factors)
+                l2 = logits * np.log2(np.e)
+                off = stage_offsets_of(l2)
+                wk = np.where(a, np.exp2(np.where(a, l2, 0.0) - off), 0.0)
+                back = np.exp2(off - m * np.log2(np.e))
+            else:
+                wk, back = pt, 1.0
             l = pt.sum(axis=1, keepdims=True)
             l1 = np.where(l > 0, l, 1.0)
             p = pt / l1
@@ -73,16 +108,16 @@ def model_backward(w, dropout_p=0.0, seed=0, residual=False):
             else:
                 zf = 1.0
             dp = (do[qa:qb, h] @ v[ka:kb, g].T) * zf
-            if thr > 0 and residual:
-                z_hi = bf16(pt * zf)
-                z_lo = bf16(pt * zf - z_hi)
-                of = (z_hi @ v[ka:kb, g] + z_lo @ v[ka:kb, g]) / l1   # the forward's fp32 O
+            if residual:
+                z_hi = bf16(wk * zf)
+                z_lo = bf16(wk * zf - z_hi)
+                of = ((z_hi + z_lo) * back) @ v[ka:kb, g] / l1       # the forward's fp32 O
                 o = bf16(of) + bf16(of - bf16(of))              # stored output + residual
                 dd = (do[qa:qb, h] * o).sum(axis=1)
             elif thr > 0:
                 dd = (p * dp).sum(axis=1)                       # the dropout path's exact D
             else:
-                o = bf16((bf16(pt) @ v[ka:kb, g]) / l1)        # the stored forward output
+                o = bf16((bf16(wk) * back) @ v[ka:kb, g] / l1)    # the stored output
                 dd = (do[qa:qb, h] * o).sum(axis=1)
             ds = bf16(p * (dp - dd[:, None]))
             z = bf16(p * zf)

@@ -225,6 +225,93 @@ def test_unequal_lengths_full_size(case):
         assert_close(gv[krows][:, g], rv, *tol, f"dV {tag}")
 
 
+def scale_workload(scale):
+    """GQA 4:2, bottom-right, d=128, ragged lengths (300/300, 129/500, 70/64) at a given scale."""
+    return wl.random_workload((66, int(abs(scale) * 1000)), [300, 129, 70], [300, 500, 64], 4,
+                              2, 128, "bf16", wl.MASK_CAUSAL_BOTTOM_RIGHT, with_dout=True,
+                              name="scale-bf16", scale=scale)
+
+
+def check_grads_derived(w, got, ref, what, residual):
+    """Gradients against the oracle at atol = max(2e-2, 1.1 x what the CPU rounding model of
+    the same route needs on these inputs), rtol 2e-2; prints the kernel's own need."""
+    from rounding_model import model_backward, required_atol
+    with np.errstate(over="ignore"):
+        model = model_backward(w, residual=residual)
+    for name, g, m, r in zip(("dQ", "dK", "dV"), got, model, ref):
+        g = to_np(g)
+        atol = max(BF16_TOL[0], 1.1 * required_atol(m, r))
+        print(f"{what} {name}: kernel needs atol {required_atol(g, r):.4f}, model "
+              f"{required_atol(m, r):.4f}, bound {atol:.4f}", flush=True)
+        assert_close(g, r, atol, BF16_TOL[1], f"{what} {name}")
+
+
+@pytest.mark.parametrize("scale", [50.0, 1e-3, -2.0])
+def test_unusual_scales_bf16(scale):
+    """The bf16 forward and backward at extreme scales: 50 makes each row's weights nearly
+    one-hot (logit gaps of hundreds, so the running offset moves at almost every stage), 1e-3
+    nearly uniform, and a negative scale folds its sign into Q. Forward against the oracle at
+    the standard bounds. Gradients grow with |scale| while the bf16 rounding of the stored
+    output, from which D = rowsum(dO * O) is formed, does not cancel in dS = P (dP - D): at
+    scale 50 the rounding model needs atol ~6 for dQ. So each route is held to the bound its
+    model derives: attn_bwd (D from the stored output), and the output-residual route
+    (attn_fwd_dropout / attn_bwd_dropout at p = 0 with out_residual: D from the unrounded
+    output), whose need at scale 50 is about a hundred times smaller."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    w = scale_workload(scale)
+    t = to_device(w)
+    with np.errstate(over="ignore"):
+        ref_o, ref_l = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode)
+        ref_g = _oracle_bwd(w)
+    out, lse = run_fwd(w, t)
+    assert_close(to_np(out), ref_o, *BF16_TOL, f"scale {scale} O")
+    assert_close(to_np(lse), ref_l, 1e-3, 0.0, f"scale {scale} LSE")
+    check_grads_derived(w, run_bwd(w, t, out, lse), ref_g, f"scale {scale}", False)
+    args = (t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
+            w.window, 0.0, 9)
+    res = torch.full_like(t["q"], float("nan"))
+    out_r, lse_r = eat.attn_fwd_dropout(t["q"], t["k"], t["v"], *args, out_residual=res)
+    assert_close(to_np(out_r), ref_o, *BF16_TOL, f"scale {scale} residual-route O")
+    assert_close(to_np(lse_r), ref_l, 1e-3, 0.0, f"scale {scale} residual-route LSE")
+    # The residual is at most half a bf16 spacing of out, and out + residual is the kernel's
+    # unrounded output: its mean error is far below that of out alone. (Its largest error
+    # grows with |scale|, which multiplies the fp32 rounding of the logits: 1.7e-4 at 50.)
+    mag = out_r.view(torch.int16) & 0x7FFF
+    up = (mag + 1).view(torch.bfloat16).float() - mag.view(torch.bfloat16).float()
+    assert torch.all(res.float().abs() <= 0.5 * up)
+    o64 = to_np(out_r).astype(np.float64)
+    err_o, err_or = np.abs(o64 - ref_o).mean(), np.abs(o64 + to_np(res) - ref_o).mean()
+    print(f"scale {scale}: mean abs error of out {err_o:.3e}, of out + residual {err_or:.3e}")
+    assert err_or < err_o / 16
+    g = eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out_r, lse_r, t["dout"], *args,
+                             out_residual=res)
+    check_grads_derived(w, g, ref_g, f"scale {scale} residual route", True)
+
+
+def test_value_offsets_residual_route():
+    """16 short causal sequences (GQA 8:2) whose values carry the ragged workload's
+    per-sequence offsets v (s + 1) + 10 s (outputs up to ~200): through attn_bwd the stored
+    output's rounding moves dQ and dK by ~2 (the model's derived need); through the
+    output-residual route (p = 0 with out_residual) D comes from the unrounded output and the
+    need drops below 0.1. Both against the oracle at their routes' derived bounds."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    from test_tolerance_derivation import offset_pack_workload
+    w = offset_pack_workload(True)
+    t = to_device(w)
+    ref_g = _oracle_bwd(w)
+    out, lse = run_fwd(w, t)
+    check_grads_derived(w, run_bwd(w, t, out, lse), ref_g, "offsets attn_bwd", False)
+    args = (t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
+            w.window, 0.0, 9)
+    res = torch.full_like(t["q"], float("nan"))
+    out_r, lse_r = eat.attn_fwd_dropout(t["q"], t["k"], t["v"], *args, out_residual=res)
+    g = eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out_r, lse_r, t["dout"], *args,
+                             out_residual=res)
+    check_grads_derived(w, g, ref_g, "offsets residual route", True)
+
+
 def test_ragged_gqa_bwd_full_size():
     """The packed ragged GQA workload's packing (16384 tokens, lengths U[1,4096] plus 63, 64,
     65, 127, 128, 129; Hq=32, Hkv=8, d=128, causal) with a loss gradient: GPU forward and
