@@ -312,6 +312,44 @@ def test_value_offsets_residual_route():
     check_grads_derived(w, g, ref_g, "offsets residual route", True)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode,window", [(1, 0), (2, 0), (0, 0), (1, 70), (2, 33)])
+def test_residual_route_edges(d, mode, window):
+    """The output-residual route at p = 0 (attn_fwd_dropout / attn_bwd_dropout with
+    out_residual) on the backward's ragged edge lengths, GQA 4:2, every alignment and two
+    windows: O and LSE at the standard bounds, out + residual far closer to the oracle than
+    out, rows with no allowed key +0.0 in out and residual, and the gradients against the
+    oracle at the model-derived bound of this route."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    lq = [0, 1, 63, 64, 65, 127, 128, 129, 200, 7]
+    lk = [5, 129, 128, 64, 63, 1, 300, 129, 0, 70]
+    w = wl.random_workload((21, d, mode), lq, lk, 4, 2, d, "bf16", mode, window,
+                           with_dout=True, name="bwd-edge")
+    print(f"residual route edges d={d} mode={mode} window={window}", flush=True)
+    t = to_device(w)
+    ref_o, ref_l = oracle.attention(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.mask_mode,
+                                    w.window)
+    args = (t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
+            w.window, 0.0, 3)
+    res = torch.full_like(t["q"], float("nan"))
+    out, lse = eat.attn_fwd_dropout(t["q"], t["k"], t["v"], *args, out_residual=res)
+    assert_close(to_np(out), ref_o, *BF16_TOL, "residual route O")
+    assert_close(to_np(lse), ref_l, 1e-3, 0.0, "residual route LSE")
+    o64 = to_np(out).astype(np.float64)
+    err_o, err_or = np.abs(o64 - ref_o).mean(), np.abs(o64 + to_np(res) - ref_o).mean()
+    assert err_or < err_o / 16, (err_o, err_or)
+    empty = ~oracle.explicit_mask(w.cu_q, w.cu_k, w.mask_mode, w.window).any(axis=1)
+    if empty.any():
+        rows = torch.from_numpy(np.nonzero(empty)[0]).cuda()
+        assert torch.all(out[rows].view(torch.int16) == 0)
+        assert torch.all(res[rows].view(torch.int16) == 0)
+    g = eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out, lse, t["dout"], *args,
+                             out_residual=res)
+    check_grads_derived(w, g, _oracle_bwd(w), f"residual route d={d} mode={mode} w={window}",
+                        True)
+
+
 def test_ragged_gqa_bwd_full_size():
     """The packed ragged GQA workload's packing (16384 tokens, lengths U[1,4096] plus 63, 64,
     65, 127, 128, 129; Hq=32, Hkv=8, d=128, causal) with a loss gradient: GPU forward and
