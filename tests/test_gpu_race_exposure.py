@@ -98,12 +98,13 @@ def test_splitk_race_exposure(poison_lib, dtype, nq, group, splits):
 
 # Backward workloads whose gradient bounds are derived on the CPU by the rounding model
 # (tests/test_tolerance_derivation.py): the seed-21 edges stay inside the standard bound,
-# the seed-42 dropout edges need DROPOUT_GRAD_TOL. The last flag runs the dropout forward
-# that also writes the output residual (its second PV contraction) and the backward that
-# forms D from it.
+# the seed-42 dropout edges need DROPOUT_GRAD_TOL. The last flag runs the forward that also
+# writes the output residual (its second PV contraction) and the backward that forms D from
+# it, with dropout or (p = 0) without.
 BWD_CASES = [(64, 1, 0, 0.0, False), (128, 2, 0, 0.0, False), (128, 0, 0, 0.0, False),
              (64, 1, 70, 0.0, False), (64, 1, 0, 0.2, False), (128, 2, 0, 0.2, False),
-             (128, 1, 70, 0.2, False), (64, 1, 0, 0.2, True), (128, 0, 0, 0.2, True)]
+             (128, 1, 70, 0.2, False), (64, 1, 0, 0.2, True), (128, 0, 0, 0.2, True),
+             (64, 2, 33, 0.0, True), (128, 1, 0, 0.0, True)]
 
 
 @pytest.mark.parametrize("d,mode,window,dropout_p,residual", BWD_CASES)
@@ -123,7 +124,7 @@ def test_backward_race_exposure(poison_lib, d, mode, window, dropout_p, residual
             w.scale, w.mask_mode, w.window)
 
     def run():
-        if dropout_p == 0.0:
+        if dropout_p == 0.0 and not residual:
             out, lse = eat.attn_fwd(*args)
             g = eat.attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], *args[3:])
         else:
