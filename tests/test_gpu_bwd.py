@@ -350,6 +350,44 @@ def test_residual_route_edges(d, mode, window):
                         True)
 
 
+def test_residual_route_train_full_size():
+    """The output-residual route at p = 0 on the training workload (B=2, Hq=32, Hkv=8,
+    N=8192, d=128, top-left): the unpipelined forward writing the residual over 65-stage
+    loops, and the backward forming D from it. Two (sequence, K/V group) slices (O, LSE of
+    the group's 4 query heads; dQ, dK, dV) against the oracle at the standard bounds."""
+    import torch
+    import exact_attention_tiled_amd as eat
+    import oracle_pool as op
+    w = wl.train_bf16()
+    t = to_device(w)
+    print("residual route train full size", flush=True)
+    args = (t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k, w.scale, w.mask_mode,
+            w.window, 0.0, 5)
+    res = torch.full_like(t["q"], float("nan"))
+    out, lse = eat.attn_fwd_dropout(t["q"], t["k"], t["v"], *args, out_residual=res)
+    dq, dk, dv = eat.attn_bwd_dropout(t["q"], t["k"], t["v"], out, lse, t["dout"], *args,
+                                      out_residual=res)
+    o, l, gq, gk, gv = (to_np(x) for x in (out, lse, dq, dk, dv))
+    del t, res, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    slices = [(0, 6), (1, 1)]
+    grp = w.hq // w.hkv
+    tasks = []
+    for s, g in slices:
+        heads = list(range(g * grp, (g + 1) * grp))
+        tasks += [(op.fwd_slice, (s, heads)), (op.bwd_slice, (s, g))]
+    refs = op.run("train_bf16", {}, tasks)
+    for i, (s, g) in enumerate(slices):
+        heads = list(range(g * grp, (g + 1) * grp))
+        rows = slice(int(w.cu_q[s]), int(w.cu_q[s + 1]))
+        (ro, rl), (rq, rk, rv) = refs[2 * i], refs[2 * i + 1]
+        assert_close(o[rows][:, heads], ro, *BF16_TOL, f"residual route O s{s} g{g}")
+        assert_close(l[heads][:, rows], rl, 1e-3, 0.0, f"residual route LSE s{s} g{g}")
+        assert_close(gq[rows][:, heads], rq, *BF16_TOL, f"residual route dQ s{s} g{g}")
+        assert_close(gk[rows][:, g], rk, *BF16_TOL, f"residual route dK s{s} g{g}")
+        assert_close(gv[rows][:, g], rv, *BF16_TOL, f"residual route dV s{s} g{g}")
+
+
 def test_ragged_gqa_bwd_full_size():
     """The packed ragged GQA workload's packing (16384 tokens, lengths U[1,4096] plus 63, 64,
     65, 127, 128, 129; Hq=32, Hkv=8, d=128, causal) with a loss gradient: GPU forward and
