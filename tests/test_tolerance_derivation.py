@@ -17,7 +17,7 @@ import numpy as np
 import oracle
 import workloads as wl
 from gpu_util import DROPOUT_GRAD_TOL, GQA64_GRAD_TOL
-from rounding_model import bf16 as _bf16, model_backward, required_atol
+from rounding_model import bf16 as _bf16, model_backward, required_atol, stage_offsets_of
 
 
 def gqa64_workload():
@@ -206,3 +206,22 @@ def test_output_residual_restores_d_without_dropout():
             assert max(resid) <= bound and max(resid[0], resid[1]) < 0.02 * min(plain[:2])
         else:
             assert max(resid[0], resid[1]) < 0.1 * min(plain[0], plain[1])
+
+
+def test_stage_offsets_follow_the_lazy_rescale_rule():
+    """The model's running offsets on hand-worked rows (stages of 2 keys, threshold 8, log2
+    units): row 0 takes stage 0's maximum 1 and keeps it (stage 1's 3 is within 8); row 1 has
+    no allowed key (its row maximum, 0, everywhere); row 2 takes 5, then moves to 20 (more
+    than 8 above); row 3 skips a fully excluded first stage and takes -4 from stage 1."""
+    ninf = -np.inf
+    x = np.array([[0.0, 1.0, ninf, 3.0],
+                  [ninf, ninf, ninf, ninf],
+                  [5.0, ninf, ninf, 20.0],
+                  [ninf, ninf, -4.0, -6.0]])
+    want = np.array([[1.0, 1.0, 3.0, 1.0],
+                     [0.0, 0.0, 0.0, 0.0],
+                     [5.0, 20.0, 20.0, 20.0],
+                     [-4.0, -4.0, -4.0, -4.0]])
+    got = stage_offsets_of(x, stage=2)
+    # excluded pairs carry the row maximum; allowed pairs their stage's offset
+    assert np.array_equal(got, want), got
