@@ -299,6 +299,23 @@ def test_unusual_scales(scale):
         check_fwd(w, out, lse, ref_o, ref_l, f"scale {scale} path {path}")
 
 
+@pytest.mark.parametrize("scale", [50.0, 1e-3, -2.0])
+def test_extreme_scales_splitk_bf16(scale):
+    """The bf16 split-K decode forward at extreme scales (GQA 4:2, 1 to 16 queries over 2 to
+    3000 keys, bottom-right): scale 50 gives logit gaps of hundreds, so a chunk's running
+    offset moves at almost every 128-key stage and the log-sum-exp merge of the chunks
+    combines partials whose maxima differ by hundreds; 1e-3 gives nearly uniform weights.
+    Automatic and 3 splits, against the oracle at the standard bounds."""
+    w = wl.random_workload((67, int(abs(scale) * 1000)), [1, 4, 16, 3], [3000, 129, 1000, 2],
+                           8, 2, 128, "bf16", wl.MASK_CAUSAL_BOTTOM_RIGHT, name="scale-splitk",
+                           scale=scale)
+    with np.errstate(over="ignore"):
+        ref_o, ref_l = _oracle(w)
+    for splits in (0, 3):
+        out, lse = run_fwd(w, path=SPLITK, num_splits=splits)
+        check_fwd(w, out, lse, ref_o, ref_l, f"split-K scale {scale} splits {splits}")
+
+
 # ----------------------------------------------------------------------------------------
 # the named workloads at full size (oracle on sampled sequences / heads)
 # ----------------------------------------------------------------------------------------
