@@ -58,7 +58,18 @@ def stage_offsets_of(logits2, stage=64, threshold=8.0):
     return off
 
 
-def model_backward(w, dropout_p=0.0, seed=0, residual=False, stage_offsets=True):
+def fp32_dot_sigma(qh, kg, chunk=16):
+    """Standard deviation of the fp32 accumulation error of every dot product q_i . k_j:
+    the matrix cores sum `chunk` exact bf16 products per instruction and round each partial
+    sum into the fp32 accumulator once (error uniform within half an ulp, standard deviation
+    2^-24 |partial| / sqrt(3))."""
+    prod = qh[:, None, :] * kg[None, :, :]
+    parts = np.cumsum(prod.reshape(prod.shape[0], prod.shape[1], -1, chunk).sum(axis=3), axis=2)
+    return 2.0 ** -24 / np.sqrt(3.0) * np.sqrt((parts ** 2).sum(axis=2))
+
+
+def model_backward(w, dropout_p=0.0, seed=0, residual=False, stage_offsets=True,
+                   logit_noise=None):
     """(dQ, dK, dV) of the rounding model for workload w (bf16 inputs, any mask, GQA). With
     residual=True (with or without dropout) D is formed from the stored output plus its bf16
     rounding residual; the forward that writes the residual splits each weight Z into
@@ -67,7 +78,13 @@ def model_backward(w, dropout_p=0.0, seed=0, residual=False, stage_offsets=True)
     stored output without. The forward's weights are rounded relative to the row maximum,
     or with stage_offsets at the running offset the prefill kernels use (stage_offsets_of):
     where one weight dominates a row (large |scale|) its rounding is exact at the row
-    maximum but not at another offset, and the stored output's rounding grows."""
+    maximum but not at another offset, and the stored output's rounding grows.
+    With logit_noise (a seed) the dot products also carry a draw of the fp32 accumulation
+    error (fp32_dot_sigma): one draw for the forward's weights and another for the
+    backward's recomputed P, normalised with the forward's LSE. Multiplied by a large
+    |scale| that error moves some weights across a bf16 rounding boundary, so the rows whose
+    stored output rounds differently vary from draw to draw; the kernel's need is then one
+    sample of the model's distribution over draws."""
     q, k, v, do = (np.asarray(a, np.float64) for a in (w.q, w.k, w.v, w.dout))
     thr = oracle.dropout_threshold(dropout_p)
     zscale = float(np.float32(256.0 / (256 - thr))) if thr > 0 else 1.0
@@ -78,6 +95,7 @@ def model_backward(w, dropout_p=0.0, seed=0, residual=False, stage_offsets=True)
     dv = np.zeros_like(v)
     sq, pq, lq = oracle.token_metadata(w.cu_q)
     sk, pk, lk = oracle.token_metadata(w.cu_k)
+    rng = np.random.default_rng(logit_noise) if logit_noise is not None else None
     for s in range(len(lq)):
         qa, qb, ka, kb = (int(x) for x in (w.cu_q[s], w.cu_q[s + 1], w.cu_k[s], w.cu_k[s + 1]))
         if qa == qb or ka == kb:
@@ -87,7 +105,13 @@ def model_backward(w, dropout_p=0.0, seed=0, residual=False, stage_offsets=True)
         rows = a.any(axis=1)
         for h in range(hq):
             g = h // grp
-            logits = np.where(a, w.scale * q[qa:qb, h] @ k[ka:kb, g].T, -np.inf)
+            dots = q[qa:qb, h] @ k[ka:kb, g].T
+            dots_b = dots
+            if rng is not None:
+                sig = fp32_dot_sigma(q[qa:qb, h], k[ka:kb, g])
+                dots = dots + rng.standard_normal(dots.shape) * sig
+                dots_b = dots_b + rng.standard_normal(dots.shape) * sig
+            logits = np.where(a, w.scale * dots, -np.inf)
             m = np.where(rows, logits.max(axis=1, initial=-np.inf), 0.0)[:, None]
             pt = np.where(a, np.exp(logits - m), 0.0)
             if stage_offsets:
@@ -101,7 +125,11 @@ def model_backward(w, dropout_p=0.0, seed=0, residual=False, stage_offsets=True)
                 wk, back = pt, 1.0
             l = pt.sum(axis=1, keepdims=True)
             l1 = np.where(l > 0, l, 1.0)
-            p = pt / l1
+            if rng is not None:
+                lse = m + np.log(l1)
+                p = np.where(a, np.exp(np.where(a, w.scale * dots_b, 0.0) - lse), 0.0)
+            else:
+                p = pt / l1
             if thr > 0:
                 keep = oracle.dropout_keep(seed, s, h, pq[qa:qb, None], pk[None, ka:kb], thr)
                 zf = np.where(keep, zscale, 0.0)
