@@ -61,11 +61,12 @@ def stage_offsets_of(logits2, stage=64, threshold=8.0):
 def fp32_dot_sigma(qh, kg, chunk=16):
     """Standard deviation of the fp32 accumulation error of every dot product q_i . k_j:
     the matrix cores sum `chunk` exact bf16 products per instruction and round each partial
-    sum into the fp32 accumulator once (error uniform within half an ulp, standard deviation
-    2^-24 |partial| / sqrt(3))."""
+    sum into the fp32 accumulator once (error uniform within half an ulp of that partial
+    sum, standard deviation ulp / sqrt(12))."""
     prod = qh[:, None, :] * kg[None, :, :]
     parts = np.cumsum(prod.reshape(prod.shape[0], prod.shape[1], -1, chunk).sum(axis=3), axis=2)
-    return 2.0 ** -24 / np.sqrt(3.0) * np.sqrt((parts ** 2).sum(axis=2))
+    ulp = np.spacing(np.abs(parts).astype(np.float32)).astype(np.float64)
+    return np.sqrt((ulp ** 2).sum(axis=2) / 12.0)
 
 
 def model_backward(w, dropout_p=0.0, seed=0, residual=False, stage_offsets=True,
